@@ -1,0 +1,222 @@
+/*
+ * vocab_ce.h -- C ABI of libvocab_ce.so: numerically stable softmax
+ * cross-entropy forward and backward over a logits matrix [T, V] on one
+ * AMD Instinct MI355X (gfx950) GPU.
+ *
+ * What is computed, per row r with target t (ignore_index rows excepted):
+ *
+ *   m   = max over non-target columns of z          (the stabilising shift)
+ *   s   = sum over non-target columns of exp(z_j - m)
+ *   x   = (m - z_t) + log s                          (= lse_{j != t} - z_t)
+ *   nll = softplus(x)                                (= -log p_t)
+ *   lse = z_t + nll
+ *   loss_r = (1 - eps) nll + eps (lse - mean_j z_j)  (eps: label smoothing)
+ *   grad_rj = k_r (p_j - eps/V)              j != t, p_j = exp(z_j - lse)
+ *   grad_rt = k_r (g_t + eps (V-1)/V),  g_t = p_t - 1 if p_t < 1/4, else -p_nt
+ *
+ * with k_r = grad_output (sum), grad_output / N_valid (mean) or
+ * grad_output[r] (none).
+ *
+ *   torchtitan PR "[loss] fix softmax collapse with improved ce perf":
+ *     opening summary -- the forward computes the non-target mass and
+ *       prepares the backward instead of saving log-probabilities;
+ *     Numerics -- NLL = softplus(lse over non-targets - z_t) with the target
+ *       dropped before the sum; target gradient p_t - 1 below p_t = 1/4,
+ *       else minus the non-target probability; ignored labels are targets
+ *       on no shard and get zero loss and gradient;
+ *     Memory/perf -- input logits are never modified; bf16 logits are
+ *       upcast inside, never copied to fp32; the forward reads the logits
+ *       once and the backward rebuilds the gradient in one pass.
+ *   Megatron-core core.tensor_parallel.cross_entropy:
+ *     VocabParallelCrossEntropy -- per-shard max, per-shard target logit
+ *       (zero where the shard does not own the target), sums combined over
+ *       the vocabulary shards; scale_gradients_inplace scales by grad_output;
+ *     vocab_parallel_cross_entropy -- label_smoothing in [0, 1); logits are
+ *       [sequence, batch, vocab / ranks], flattened here to T rows.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument not marked "host" is a DEVICE pointer.  The
+ *     caller owns and allocates every buffer; the library never allocates,
+ *     frees or synchronises, and launches all work on `stream` (a
+ *     hipStream_t; NULL is the default stream).  Calls are asynchronous.
+ *   - Inputs are const and never written.  Outputs must not overlap inputs
+ *     or each other.
+ *   - Logits: row r, column j of this call lives at logits[r * ld + j]
+ *     (elements, not bytes), j in [0, V_local).  Any alignment is accepted;
+ *     16-byte aligned rows take the vectorised path.
+ *   - Targets are int64 [T]; a target equal to ignore_index marks an
+ *     ignored row; any other target outside [0, V_total) is a bad target.
+ *   - Return value: CE_OK (0) or a negative ce_status.  Arguments are
+ *     checked on the host before anything is launched; a failed check
+ *     launches nothing.  CE_ERR_HIP reports a failed launch.
+ *   - Bad targets are data errors found on the device: such a row gets
+ *     status -1, loss_r = NaN (so a sum or mean over it is NaN) and a
+ *     gradient row of zeros, and is counted in *err_count.
+ *   - T == 0 is a successful no-op except that scalar outputs are written
+ *     (loss 0 for sum, NaN for mean, n_valid 0, err_count 0).
+ *   - Results are deterministic: fixed reduction trees, no float atomics.
+ */
+#ifndef VOCAB_CE_H
+#define VOCAB_CE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CE_F32 = 0,  /* IEEE binary32 */
+    CE_BF16 = 1  /* bfloat16: the top 16 bits of a binary32; outputs are
+                    rounded to nearest, ties to even */
+} ce_dtype;
+
+typedef enum {
+    CE_RED_NONE = 0, /* per-row losses only; k_r = grad_output[r] */
+    CE_RED_SUM = 1,  /* loss = sum over non-ignored rows; k_r = grad_output[0] */
+    CE_RED_MEAN = 2  /* loss = that sum / N_valid; k_r = grad_output[0] / N_valid */
+} ce_reduction;
+
+typedef enum {
+    CE_OK = 0,
+    CE_ERR_NULL = -1,      /* a required pointer is NULL */
+    CE_ERR_SHAPE = -2,     /* T < 0, V_local < 1, ld < V_local, ldg < V_local,
+                              vocab_start < 0, vocab_start + V_local > V_total,
+                              or a size too large for the kernels' indexing */
+    CE_ERR_SMOOTHING = -3, /* label_smoothing not in [0, 1) or not finite */
+    CE_ERR_DTYPE = -4,     /* unknown ce_dtype */
+    CE_ERR_REDUCTION = -5, /* unknown ce_reduction */
+    CE_ERR_WORKSPACE = -6, /* workspace NULL or smaller than ce_workspace_bytes */
+    CE_ERR_SHARDS = -7,    /* n_shards < 1 or > CE_MAX_SHARDS */
+    CE_ERR_ALIAS = -8,     /* grad overlaps logits */
+    CE_ERR_HIP = -9,       /* a HIP launch failed */
+    CE_ERR_ARG = -10       /* an output given where the call cannot produce it
+                              (e.g. finalize outputs of a split-vocabulary
+                              ce_forward, or the whole-vocabulary fused call
+                              given a shard) */
+} ce_status;
+
+#define CE_MAX_SHARDS 64
+
+/* The problem one call works on.  A host struct, passed by pointer. */
+typedef struct {
+    int64_t T;            /* rows */
+    int64_t V_local;      /* columns handled by this call */
+    int64_t ld;           /* row stride of the logits, in elements (>= V_local) */
+    int64_t vocab_start;  /* global column of this call's column 0 */
+    int64_t V_total;      /* vocabulary size across all shards */
+    int64_t ignore_index; /* target value that marks an ignored row, e.g. -100 */
+    float label_smoothing;/* eps in [0, 1) */
+    int32_t reduction;    /* ce_reduction */
+} ce_problem;
+
+/* Partial statistics of one row over this call's columns (one vocabulary
+ * shard): the forward's output when the vocabulary is split, merged by
+ * ce_merge_shard_stats.  32 bytes, device memory, [T] per shard.  A row
+ * whose target is ignore_index or outside [0, V_total) is not read: its
+ * statistics are m = -inf, s = 0, zt = 0, own = 0, sz = 0. */
+typedef struct {
+    float m;          /* max over this shard's non-target columns; -inf if none */
+    float zt;         /* z at the target if this shard owns it, else 0 */
+    int32_t own;      /* 1 if this shard owns the target, else 0 */
+    int32_t reserved; /* 0 */
+    double s;         /* sum over the same columns of exp(z_j - m); 0 if m = -inf */
+    double sz;        /* sum of z over all of this shard's columns; computed
+                         only when label_smoothing > 0 (else 0) */
+} ce_row_stats;
+
+/* What the forward prepares for the backward, per row.  24 bytes, device
+ * memory, [T]. */
+typedef struct {
+    double lse;     /* log-sum-exp of the whole row (all shards) */
+    double gt;      /* target gradient before the row scale k_r: p_t - 1 or
+                       -p_nt by the 1/4 select, plus eps (V-1)/V */
+    float m;        /* the merged non-target max */
+    int32_t status; /* 1 valid, 0 ignored, -1 bad target */
+} ce_row_final;
+
+/* Workspace, in bytes, that `op` needs for `prob` (0 if none).  `op` is one
+ * of the CE_OP_* values.  Host function; never fails (an invalid problem
+ * yields 0 and the entry point then reports the problem's error). */
+enum { CE_OP_FORWARD = 0, CE_OP_BACKWARD = 1, CE_OP_FUSED = 2, CE_OP_MERGE = 3 };
+size_t ce_workspace_bytes(const ce_problem *prob, int op);
+
+/* Forward: one read of the logits.
+ *   stats   [T] out, required: this call's partial row statistics.
+ *   When the call covers the whole vocabulary (vocab_start == 0 and
+ *   V_local == V_total) it also finalizes, writing whichever of these are
+ *   non-NULL:
+ *     fin       [T] ce_row_final for ce_backward;
+ *     loss_rows [T] float per-row loss (+0 ignored, NaN bad target);
+ *     loss      [1] float reduced loss (sum or mean; not written for none);
+ *     n_valid   [1] int32 number of rows with status 1;
+ *     err_count [1] int32 number of bad targets.
+ *   When the vocabulary is split, those outputs must be NULL and
+ *   ce_merge_shard_stats produces them from all shards' stats.
+ *   ws/ws_bytes: workspace of at least ce_workspace_bytes(prob, CE_OP_FORWARD).
+ * Megatron-core VocabParallelCrossEntropy.calculate_logits_max and
+ * gather_predicted_logits (per-shard max and owned target logit);
+ * torchtitan PR Numerics (non-target mass, target dropped before the sum). */
+int ce_forward(const ce_problem *prob, const void *logits, int logits_dtype,
+               const int64_t *target, ce_row_stats *stats, ce_row_final *fin,
+               float *loss_rows, float *loss, int32_t *n_valid, int32_t *err_count,
+               void *ws, size_t ws_bytes, void *stream);
+
+/* Merge the partial statistics of n_shards vocabulary shards, in shard
+ * order 0..n_shards-1, and finalize:
+ *   M = max_s m_s;  s = sum_s s_s exp(m_s - M);  zt = sum_s zt_s;
+ *   own = sum_s own_s (a non-ignored row is valid only if own == 1);
+ *   sz = sum_s sz_s;  then x, nll, lse, loss_r, the target select.
+ *   shard_stats [n_shards][T], shard-major (shard k's row r at k * T + r).
+ *   prob->V_total is the full vocabulary; V_local, ld, vocab_start unused.
+ *   fin [T] required; loss_rows, loss, n_valid, err_count optional.
+ *   ws/ws_bytes: at least ce_workspace_bytes(prob, CE_OP_MERGE).
+ * On one GPU this replaces the vocabulary-parallel all-reduce of
+ * Megatron-core vocab_parallel_cross_entropy (tp_group). */
+int ce_merge_shard_stats(const ce_problem *prob, int n_shards,
+                         const ce_row_stats *shard_stats, const int64_t *target,
+                         ce_row_final *fin, float *loss_rows, float *loss,
+                         int32_t *n_valid, int32_t *err_count, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* Backward: one read of the logits and one write of the gradient.
+ *   fin         [T] from ce_forward (unsharded) or ce_merge_shard_stats.
+ *   n_valid     [1] device int32, required for CE_RED_MEAN (else may be NULL).
+ *   grad_output device float: [1] for sum and mean, [T] for none; NULL
+ *               means 1.0 everywhere.
+ *   grad        [T, V_local] out, row stride ldg elements, grad_dtype;
+ *               must not overlap the logits (CE_ERR_ALIAS).
+ * Ignored and bad-target rows get +0 everywhere.
+ * Megatron-core VocabParallelCrossEntropy.prepare_gradient_calculation_operands,
+ * calculate_gradients, scale_gradients_inplace; torchtitan PR Numerics
+ * (target select) and Memory/perf (one fused gradient pass). */
+int ce_backward(const ce_problem *prob, const void *logits, int logits_dtype,
+                const int64_t *target, const ce_row_final *fin, const int32_t *n_valid,
+                const float *grad_output, void *grad, int grad_dtype, int64_t ldg,
+                void *stream);
+
+/* Fused forward + backward over the whole vocabulary (vocab_start == 0,
+ * V_local == V_total): reads each logits row once and writes its gradient
+ * once.  loss_rows, loss, n_valid, err_count optional (loss is not written
+ * for CE_RED_NONE); grad_output as in ce_backward; grad as in ce_backward.
+ * ws/ws_bytes: at least ce_workspace_bytes(prob, CE_OP_FUSED).
+ * torchtitan PR opening summary (the forward prepares the backward) and
+ * Memory/perf (one read of the logits, one fused gradient pass). */
+int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtype,
+                     const int64_t *target, const float *grad_output, float *loss_rows,
+                     float *loss, int32_t *n_valid, int32_t *err_count, void *grad,
+                     int grad_dtype, int64_t ldg, void *ws, size_t ws_bytes,
+                     void *stream);
+
+/* Human-readable name of a ce_status.  Host function, static storage. */
+const char *ce_status_str(int status);
+
+/* Library version as MAJOR * 10000 + MINOR * 100 + PATCH.  Host function. */
+int ce_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VOCAB_CE_H */

@@ -1,0 +1,84 @@
+"""The C ABI library loads and exports every function include/vocab_ce.h
+declares; host-only entry points and argument checks work without a GPU
+(every call below returns before any HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from vocab_softmax_cross_row_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vocab_ce.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ce_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from vocab_softmax_cross_row_amd import build
+        build.build()
+    return B.lib()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_sizes_match_header():
+    assert ctypes.sizeof(B.CEProblem) == 56
+    assert B.ROW_STATS_DTYPE.itemsize == B.ROW_STATS_BYTES == 32
+    assert B.ROW_FINAL_DTYPE.itemsize == B.ROW_FINAL_BYTES == 24
+
+
+def test_host_only_calls(lib):
+    assert B.ce_version() == 100
+    assert B.ce_status_str(0) == "CE_OK"
+    assert "label_smoothing" in B.ce_status_str(-3)
+    p = B.make_problem(16384, 128256)
+    assert B.ce_workspace_bytes(p, B.CE_OP_BACKWARD) == 0
+    fused = B.ce_workspace_bytes(p, B.CE_OP_FUSED)
+    assert fused >= 16384 * (32 + 24 + 4)
+    small = B.make_problem(8, 128256)   # few rows: the split-V grid needs partials
+    assert B.ce_workspace_bytes(small, B.CE_OP_FUSED) >= 8 * 32 * 2
+    bad = B.make_problem(4, 10, label_smoothing=1.5)
+    assert B.ce_workspace_bytes(bad, B.CE_OP_FUSED) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(label_smoothing=1.0), -3), (dict(label_smoothing=-0.1), -3),
+    (dict(reduction=7), -5), (dict(ld=5), -2), (dict(vocab_start=5), -2),
+])
+def test_argument_checks_before_any_launch(lib, kw, status):
+    args = dict(T=4, V_local=10)
+    args.update({k: v for k, v in kw.items() if k in ("ld",)})
+    p = B.make_problem(args["T"], args["V_local"], args.get("ld"),
+                       **{k: v for k, v in kw.items() if k != "ld"})
+    rc = lib.ce_fused_fwd_bwd(ctypes.byref(p), None, 1, None, None, None, None, None, None,
+                              None, 1, 10, None, 0, None)
+    assert rc == status
+
+
+def test_null_and_dtype_checks(lib):
+    p = B.make_problem(4, 10)
+    assert lib.ce_fused_fwd_bwd(None, None, 1, None, None, None, None, None, None, None, 1, 10,
+                                None, 0, None) == -1
+    assert lib.ce_fused_fwd_bwd(ctypes.byref(p), None, 1, None, None, None, None, None, None,
+                                None, 1, 10, None, 0, None) == -1
+    assert lib.ce_backward(ctypes.byref(p), None, 9, None, None, None, None, None, 1, 10,
+                           None) == -4
+    assert lib.ce_merge_shard_stats(ctypes.byref(p), 0, None, None, None, None, None, None,
+                                    None, None, 0, None) == -7
+    shard = B.make_problem(4, 5, vocab_start=5, V_total=10)
+    one = ctypes.c_void_p(16)
+    assert lib.ce_forward(ctypes.byref(shard), one, 1, one, one, None, one, None, None, None,
+                          None, 0, None) == -10

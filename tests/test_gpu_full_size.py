@@ -1,0 +1,110 @@
+"""GPU parity at the measured workload's full size, in the launch
+configuration the benchmark times: T = 16384 rows, V = 128256 bf16 logits
+(fused), and the same bytes as two 64128-column shards with label smoothing
+0.1 (forward per shard, on-device merge, backward per shard).
+
+The oracle recomputes a sample of rows one by one (every kind of row:
+ordinary, confident-target, ignored) and the whole-batch loss; properties
+that hold at any size cover the rest (counts, zero rows, unchanged input).
+"""
+import numpy as np
+import pytest
+import torch
+
+import vocab_softmax_cross_row_amd as vce
+from oracle import ce_oracle as O
+from synth import ce_inputs as S
+from synth.ce_inputs import to_numpy_logits
+from tests import parity_util as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def page():
+    print("[full] generating T=16384 V=128256 bf16 on the GPU", flush=True)
+    logits, target = S.generate(S.PAGE, device=DEV, block_rows=2048)
+    torch.cuda.synchronize()
+    return logits, target
+
+
+def _sample_rows(target, logits):
+    t = target.cpu().numpy()
+    rng = np.random.default_rng(2024)
+    ign = np.nonzero(t == -100)[0]
+    valid = np.nonzero(t != -100)[0]
+    # confident rows: the target logit far above the row's typical maximum
+    zt = logits[torch.arange(logits.shape[0], device=DEV),
+                torch.clamp(target, min=0)].float().cpu().numpy()
+    conf = valid[zt[valid] > 22.0]
+    rows = np.concatenate([valid[:8], rng.choice(conf, 16, replace=False),
+                           rng.choice(ign, 6, replace=False),
+                           rng.choice(valid, 12, replace=False), [t.shape[0] - 1]])
+    return np.unique(rows)
+
+
+def _checksum(x):
+    return int(x.view(torch.int16).to(torch.int64).sum().item())
+
+
+def test_fused_full_size(page):
+    logits, target = page
+    T, V = logits.shape
+    ck = _checksum(logits)
+    print("[full] fused fwd+bwd", flush=True)
+    out = vce.fused_fwd_bwd(logits, target)
+    torch.cuda.synchronize()
+    assert _checksum(logits) == ck, "logits modified"
+    t = target.cpu().numpy()
+    n_valid = int((t != -100).sum())
+    assert out["n_valid"].item() == n_valid and out["err_count"].item() == 0
+    lr = out["loss_rows"].double().cpu().numpy()
+    assert np.all(lr[t == -100] == 0.0)
+    # property: the loss is the mean of the per-row losses over valid rows
+    assert abs(out["loss"].item() - lr.sum() / n_valid) <= 1e-6 * abs(out["loss"].item())
+    rows = _sample_rows(target, logits)
+    idx = torch.from_numpy(rows).to(DEV)
+    sub_logits, sub_t = logits[idx], target[idx]
+    ref = P.oracle_for(sub_logits, sub_t, n_valid=n_valid)
+    P.assert_loss_rows(out["loss_rows"][idx], ref, "full-size sample")
+    P.assert_grad_close(out["grad"][idx], ref["grad"], "full-size sample grad")
+    conf = P.collapse_rows(sub_logits, sub_t)     # indices into the sample
+    assert len(conf) >= 8
+    P.assert_collapse_rows(out["loss_rows"][idx], out["grad"][idx].cpu(), sub_t.cpu(), ref,
+                           conf, "full-size collapse rows")
+    # the whole-batch loss from the oracle over every row
+    print("[full] oracle over all rows", flush=True)
+    z = to_numpy_logits(logits)
+    f = O.forward(z, t)
+    loss, nv, _ = O.reduce(f["loss"], f["status"], "mean")
+    assert nv == n_valid
+    P.assert_scalar_loss(out["loss"].item(), loss, "full-size loss")
+
+
+def test_split_vocabulary_full_size(page):
+    logits, target = page
+    T, V = logits.shape
+    half = V // 2
+    eps = 0.1
+    print("[full] split-V shards, eps=0.1", flush=True)
+    s1 = vce.forward(logits[:, :half], target, vocab_start=0, V_total=V, label_smoothing=eps)
+    s2 = vce.forward(logits[:, half:], target, vocab_start=half, V_total=V,
+                     label_smoothing=eps)
+    m = vce.merge_shard_stats([s1["stats"], s2["stats"]], target, V, label_smoothing=eps)
+    g1 = vce.backward(logits[:, :half], target, m["fin"], m["n_valid"], vocab_start=0,
+                      V_total=V, label_smoothing=eps)
+    g2 = vce.backward(logits[:, half:], target, m["fin"], m["n_valid"], vocab_start=half,
+                      V_total=V, label_smoothing=eps)
+    torch.cuda.synchronize()
+    t = target.cpu().numpy()
+    n_valid = int((t != -100).sum())
+    assert m["n_valid"].item() == n_valid
+    rows = _sample_rows(target, logits)
+    idx = torch.from_numpy(rows).to(DEV)
+    ref = P.oracle_for(logits[idx], target[idx], eps=eps, n_valid=n_valid)
+    P.assert_loss_rows(m["loss_rows"][idx], ref, "split full-size sample")
+    P.assert_grad_close(g1[idx], ref["grad"][:, :half], "split shard 0")
+    P.assert_grad_close(g2[idx], ref["grad"][:, half:], "split shard 1")
+    lr = m["loss_rows"].double().cpu().numpy()
+    assert abs(m["loss"].item() - lr.sum() / n_valid) <= 1e-6 * abs(m["loss"].item())

@@ -1,0 +1,362 @@
+"""GPU parity: the HIP library through its C ABI against the fp64 oracle.
+
+Sizes the oracle finishes in seconds but that span several vectors per
+thread, several workgroup shapes, a scalar tail and the split-V grid; every
+case is seeded (synth/ce_inputs.py).  Tolerances: tests/parity_util.py.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import vocab_softmax_cross_row_amd as vce
+from oracle import ce_oracle as O
+from synth import ce_inputs as S
+from synth.ce_inputs import to_numpy_logits
+from tests import parity_util as P
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _case(base, T, V, seed, **kw):
+    c = S.scaled(base, T, V, seed, **kw)
+    logits, target = S.generate(c)
+    return c, logits.to(DEV), target.to(DEV)
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _fused_check(case, logits, target, *, grad_dtype=None, grad_output=None, what=""):
+    _say(f"[fused] {what} T={case.T} V={case.V} {logits.dtype}->{grad_dtype or logits.dtype} "
+         f"eps={case.eps} red={case.reduction}")
+    before = logits.contiguous().view(torch.uint8).clone()
+    out = vce.fused_fwd_bwd(logits, target, ignore_index=case.ignore_index,
+                            label_smoothing=case.eps, reduction=case.reduction,
+                            grad_output=grad_output, grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(before, logits.contiguous().view(torch.uint8)), "logits modified"
+    ref = P.oracle_for(logits, target, ignore_index=case.ignore_index, eps=case.eps,
+                       reduction=case.reduction,
+                       grad_output=1.0 if grad_output is None else grad_output)
+    assert int(out["n_valid"].item()) == ref["n_valid"]
+    assert int(out["err_count"].item()) == ref["n_bad"]
+    P.assert_loss_rows(out["loss_rows"], ref, what)
+    if case.reduction != "none":
+        P.assert_scalar_loss(out["loss"].item(), ref["loss"], what)
+    P.assert_grad_close(out["grad"], ref["grad"], what)
+    bad = ref["status"] != 1
+    if bad.any():
+        g = out["grad"].detach().cpu()[torch.from_numpy(bad)]
+        assert torch.all(g == 0), f"{what}: non-valid rows must have zero gradient"
+    coll = P.collapse_rows(logits, target)
+    P.assert_collapse_rows(out["loss_rows"], out["grad"].cpu(), target.cpu(), ref, coll, what)
+    return out, ref
+
+
+# --------------------------------------------------------------------------
+# the named workloads, at parity size
+# --------------------------------------------------------------------------
+
+def test_tiny_workload_fp32():
+    """T=64, V=1000 fp32, 4 ignored rows, 8 rows at rowmax + 25, mean."""
+    c = S.TINY
+    logits, target = S.generate(c)
+    out, ref = _fused_check(c, logits.to(DEV), target.to(DEV), what="tiny")
+    assert len(P.collapse_rows(logits, target)) == 8
+
+
+def test_mid_workload_scaled():
+    _fused_check(*_case(S.MID, 192, 32000, 7), what="mid")
+
+
+def test_page_workload_scaled():
+    c, logits, target = _case(S.PAGE, 96, 128256, 8)
+    _fused_check(c, logits, target, what="page")
+
+
+@pytest.mark.parametrize("V", [1000, 2000, 4000, 8192, 16000, 32000, 64128, 128256])
+def test_every_resident_shape_bf16(V):
+    c, logits, target = _case(S.PAGE, 520, V, 100 + V % 97)
+    _fused_check(c, logits, target, what=f"resident V={V}")
+
+
+@pytest.mark.parametrize("V", [1000, 4000, 16000, 65536])
+def test_resident_shapes_fp32(V):
+    c, logits, target = _case(S.TINY, 520, V, 200 + V % 89)
+    _fused_check(c, logits, target, what=f"resident fp32 V={V}")
+
+
+@pytest.mark.parametrize("V", [1003, 32005, 128257])
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_ragged_tail(V, dt):
+    base = S.PAGE if dt == "bf16" else S.TINY
+    c, logits, target = _case(base, 520, V, 300 + V % 31)
+    # put targets into the scalar tail for some rows
+    target[1] = V - 1
+    target[2] = V - 2
+    _fused_check(c, logits, target, what=f"ragged {dt} V={V}")
+
+
+@pytest.mark.parametrize("in_dt,out_dt", [("bf16", torch.float32), ("f32", torch.bfloat16)])
+def test_mixed_dtypes(in_dt, out_dt):
+    base = S.PAGE if in_dt == "bf16" else S.TINY
+    c, logits, target = _case(base, 530, 5000, 41)
+    _fused_check(c, logits, target, grad_dtype=out_dt, what=f"mixed {in_dt}->{out_dt}")
+
+
+@pytest.mark.parametrize("reduction", ["none", "sum", "mean"])
+def test_reductions_and_grad_output(reduction):
+    c, logits, target = _case(S.PAGE, 520, 3000, 51, reduction=reduction)
+    if reduction == "none":
+        go = torch.randn(c.T, generator=torch.Generator().manual_seed(3)).to(DEV)
+    else:
+        go = torch.tensor([0.37], device=DEV)
+    _fused_check(c, logits, target, grad_output=go, what=f"reduction {reduction}")
+
+
+@pytest.mark.parametrize("eps", [0.1, 0.3])
+@pytest.mark.parametrize("V", [1000, 32000, 128256])
+def test_label_smoothing_fused(eps, V):
+    c, logits, target = _case(S.PAGE, 520, V, 61, eps=eps)
+    _fused_check(c, logits, target, what=f"smoothing eps={eps} V={V}")
+
+
+def test_label_smoothing_fp32_out():
+    c, logits, target = _case(S.TINY, 520, 1500, 62, eps=0.2, reduction="sum")
+    _fused_check(c, logits, target, what="smoothing fp32 sum")
+
+
+def test_split_v_grid_short_T():
+    """Few rows, long rows: the fused entry point splits every row into
+    column chunks (partial statistics merged on the device)."""
+    c, logits, target = _case(S.PAGE, 24, 128256, 71)
+    _fused_check(c, logits, target, what="split-V grid")
+    c, logits, target = _case(S.PAGE, 24, 128256, 72, eps=0.1)
+    _fused_check(c, logits, target, what="split-V grid smoothing")
+
+
+def test_unaligned_rows_take_the_scalar_path():
+    """ld not a multiple of 8 elements: rows are not 16-byte aligned."""
+    c, full, target = _case(S.PAGE, 520, 2003, 81)
+    view = full[:, :2001]        # ld = 2003, V = 2001
+    _fused_check(c, view, target, what="unaligned ld")
+    g = torch.empty((c.T, 2005), dtype=torch.bfloat16, device=DEV)[:, 1:2002]
+    out = vce.fused_fwd_bwd(view, target, grad=g)
+    torch.cuda.synchronize()
+    ref = P.oracle_for(view, target)
+    P.assert_grad_close(out["grad"], ref["grad"], "unaligned grad")
+
+
+# --------------------------------------------------------------------------
+# unfused path: forward, split-vocabulary shards, merge, backward
+# --------------------------------------------------------------------------
+
+def _stats_check(gpu_stats, ref_stats, target, V_total, what, eps):
+    """m, z_t and own exactly, s and the row sum to 1e-5 relative, on rows
+    with a valid target; rows that are ignored or have a bad target are not
+    read and carry m = -inf, s = 0, z_t = 0, own = 0, sum 0."""
+    st = vce.read_stats(gpu_stats)
+    t = np.asarray(target)
+    read = (t != -100) & (t >= 0) & (t < V_total)
+    assert np.array_equal(st["own"][read], ref_stats["own"][read]), what
+    assert np.array_equal(st["m"][read].astype(np.float64), ref_stats["m"][read]), f"{what}: m"
+    assert np.array_equal(st["zt"][read].astype(np.float64), ref_stats["zt"][read]), \
+        f"{what}: zt"
+    rs = ref_stats["s"][read]
+    rel = np.abs(st["s"][read] - rs) / np.maximum(rs, 1e-300)
+    assert rel.max(initial=0) <= 1e-5, f"{what}: s rel {rel.max():.2e}"
+    if eps > 0:   # the row sum is only formed when smoothing needs it
+        sz = ref_stats["sz"][read]
+        scale = np.maximum(np.abs(sz), 1.0)
+        assert (np.abs(st["sz"][read] - sz) / scale).max(initial=0) <= 1e-5, f"{what}: sum z"
+    skip = ~read
+    assert np.all(st["m"][skip] == -np.inf) and np.all(st["s"][skip] == 0)
+    assert np.all(st["own"][skip] == 0) and np.all(st["zt"][skip] == 0)
+
+
+@pytest.mark.parametrize("eps", [0.0, 0.1])
+def test_forward_backward_unsharded(eps):
+    c, logits, target = _case(S.PAGE, 1100, 20000, 91, eps=eps)
+    _say(f"[unfused] T={c.T} V={c.V} eps={eps}")
+    f = vce.forward(logits, target, label_smoothing=eps)
+    g = vce.backward(logits, target, f["fin"], f["n_valid"], label_smoothing=eps)
+    torch.cuda.synchronize()
+    ref = P.oracle_for(logits, target, eps=eps)
+    assert int(f["n_valid"].item()) == ref["n_valid"]
+    P.assert_loss_rows(f["loss_rows"], ref, "unfused")
+    P.assert_scalar_loss(f["loss"].item(), ref["loss"], "unfused")
+    P.assert_grad_close(g, ref["grad"], "unfused grad")
+    # statistics of the whole row
+    z = to_numpy_logits(logits)
+    t = target.cpu().numpy()
+    rs = O.shard_stats(z, t, 0)
+    _stats_check(f["stats"], rs, t, c.V, "whole-row stats", eps)
+    fin = vce.read_final(f["fin"])
+    assert np.array_equal(fin["status"], ref["status"])
+
+
+@pytest.mark.parametrize("cuts,eps,T", [([64128], 0.1, 700), ([64128], 0.0, 700),
+                                        ([40000, 90000], 0.1, 650), ([64128], 0.1, 40)])
+def test_split_vocabulary_shards(cuts, eps, T):
+    """Shards of a 128256-column vocabulary: per-shard statistics (checked
+    against the oracle's shard emulation), the on-device merge, and the
+    per-shard backward."""
+    c, logits, target = _case(S.PAGE, T, 128256, 95 + len(cuts), eps=eps)
+    V = c.V
+    edges = [0] + cuts + [V]
+    _say(f"[shards] T={T} edges={edges} eps={eps}")
+    z = to_numpy_logits(logits)
+    t = target.cpu().numpy()
+    stats = []
+    for a, b in zip(edges[:-1], edges[1:]):
+        f = vce.forward(logits[:, a:b], target, vocab_start=a, V_total=V,
+                        label_smoothing=eps)
+        stats.append(f["stats"])
+        rs = O.shard_stats(np.ascontiguousarray(z[:, a:b]), t, a)
+        torch.cuda.synchronize()
+        _stats_check(f["stats"], rs, t, V, f"shard [{a},{b})", eps)
+    m = vce.merge_shard_stats(stats, target, V, label_smoothing=eps)
+    grads = []
+    for a, b in zip(edges[:-1], edges[1:]):
+        grads.append(vce.backward(logits[:, a:b], target, m["fin"], m["n_valid"],
+                                  vocab_start=a, V_total=V, label_smoothing=eps))
+    torch.cuda.synchronize()
+    ref = P.oracle_for(logits, target, eps=eps)
+    assert int(m["n_valid"].item()) == ref["n_valid"]
+    P.assert_loss_rows(m["loss_rows"], ref, "merged")
+    P.assert_scalar_loss(m["loss"].item(), ref["loss"], "merged")
+    for (a, b), g in zip(zip(edges[:-1], edges[1:]), grads):
+        P.assert_grad_close(g, ref["grad"][:, a:b], f"shard grad [{a},{b})")
+
+
+def test_fused_equals_unfused_equals_shards_loss():
+    """Three paths to the same loss (fp32 rounding apart)."""
+    c, logits, target = _case(S.PAGE, 600, 64128, 99)
+    a = vce.fused_fwd_bwd(logits, target)
+    f = vce.forward(logits, target)
+    s1 = vce.forward(logits[:, :32064], target, vocab_start=0, V_total=64128)
+    s2 = vce.forward(logits[:, 32064:], target, vocab_start=32064, V_total=64128)
+    m = vce.merge_shard_stats([s1["stats"], s2["stats"]], target, 64128)
+    torch.cuda.synchronize()
+    la, lf, lm = a["loss"].item(), f["loss"].item(), m["loss"].item()
+    assert abs(la - lf) <= 1e-5 * abs(lf) and abs(lm - lf) <= 1e-5 * abs(lf)
+
+
+# --------------------------------------------------------------------------
+# edge cases
+# --------------------------------------------------------------------------
+
+def test_empty_batch():
+    logits = torch.empty((0, 100), dtype=torch.bfloat16, device=DEV)
+    target = torch.empty((0,), dtype=torch.int64, device=DEV)
+    out = vce.fused_fwd_bwd(logits, target)
+    torch.cuda.synchronize()
+    assert math.isnan(out["loss"].item()) and out["n_valid"].item() == 0
+    out = vce.fused_fwd_bwd(logits, target, reduction="sum")
+    torch.cuda.synchronize()
+    assert out["loss"].item() == 0.0
+
+
+def test_single_column_and_all_ignored():
+    logits = torch.randn((5, 1), device=DEV)
+    target = torch.zeros(5, dtype=torch.int64, device=DEV)
+    out = vce.fused_fwd_bwd(logits, target, label_smoothing=0.1)
+    torch.cuda.synchronize()
+    assert torch.all(out["loss_rows"] == 0) and torch.all(out["grad"] == 0)
+    logits = torch.randn((7, 300), device=DEV).to(torch.bfloat16)
+    target = torch.full((7,), -100, dtype=torch.int64, device=DEV)
+    out = vce.fused_fwd_bwd(logits, target)
+    torch.cuda.synchronize()
+    assert math.isnan(out["loss"].item()) and torch.all(out["grad"] == 0)
+
+
+def test_bad_targets_counted():
+    logits = torch.randn((8, 500), device=DEV)
+    target = torch.tensor([0, 1, 500, -1, -100, 7, 10**12, 3], dtype=torch.int64, device=DEV)
+    out = vce.fused_fwd_bwd(logits, target, reduction="sum")
+    torch.cuda.synchronize()
+    assert out["err_count"].item() == 3 and out["n_valid"].item() == 4
+    lr = out["loss_rows"].cpu()
+    assert torch.isnan(lr[[2, 3, 6]]).all() and lr[4].item() == 0.0
+    assert torch.all(out["grad"][[2, 3, 4, 6]] == 0)
+    assert math.isnan(out["loss"].item())
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_minus_inf_logits(dt):
+    """Rows with -inf fallback logits (torchtitan PR Test Plan)."""
+    g = torch.Generator().manual_seed(5)
+    z = torch.randn((520, 700), generator=g) * 2
+    target = torch.randint(0, 700, (520,), generator=g)
+    z[0, :350] = -math.inf                  # half the row at -inf
+    z[1, :] = -math.inf
+    z[1, target[1]] = 1.0                   # only the target is finite
+    z[2, target[2]] = -math.inf             # target at -inf: loss +inf
+    target[3] = -100
+    z[3, :] = -math.inf                     # ignored row of -inf
+    z = z.to(dt)
+    if z[0, target[0]] == -math.inf:
+        target[0] = 400
+    logits, tgt = z.to(DEV), target.to(DEV)
+    out = vce.fused_fwd_bwd(logits, tgt, reduction="none")
+    torch.cuda.synchronize()
+    ref = P.oracle_for(logits, tgt, reduction="none")
+    lr = out["loss_rows"].cpu()
+    assert lr[1].item() == 0.0 and torch.all(out["grad"][1] == 0)
+    assert lr[2].item() == math.inf and lr[3].item() == 0.0
+    keep = [i for i in range(520) if i != 2]
+    rows = ref["status"].copy()
+    rows[2] = 0  # the +inf row is compared exactly above
+    fake = dict(ref)
+    fake["status"] = rows
+    fake["loss_rows"] = ref["loss_rows"].copy()
+    fake["loss_rows"][2] = 0.0
+    lr2 = out["loss_rows"].clone()
+    lr2[2] = 0.0
+    P.assert_loss_rows(lr2, fake, "-inf")
+    P.assert_grad_close(out["grad"][keep], ref["grad"][keep], "-inf grad")
+    assert float(out["grad"][2, tgt[2]]) == -1.0
+
+
+def test_deterministic_run_to_run():
+    c, logits, target = _case(S.PAGE, 700, 50000, 123, eps=0.1)
+    a = vce.fused_fwd_bwd(logits, target, label_smoothing=0.1)
+    b = vce.fused_fwd_bwd(logits, target, label_smoothing=0.1)
+    torch.cuda.synchronize()
+    for k in ("loss", "loss_rows", "grad"):
+        assert torch.equal(a[k].view(torch.uint8), b[k].view(torch.uint8)), k
+
+
+def test_subnormal_gradients_round_correctly():
+    """Probabilities far below 2^-126 come out as the right subnormals (or
+    zero) in both output dtypes, not flushed early."""
+    z = torch.zeros((520, 600))
+    z[:, 1:300] = torch.linspace(-95.0, -80.0, 299)   # p ~ 1e-42 .. 1e-35
+    z[:, 300:] = torch.linspace(-110.0, -100.0, 300)  # below the smallest subnormal
+    target = torch.zeros(520, dtype=torch.int64)
+    for dt in (torch.float32, torch.bfloat16):
+        logits = z.to(dt).to(DEV)
+        tgt = target.to(DEV)
+        out = vce.fused_fwd_bwd(logits, tgt, reduction="sum")
+        torch.cuda.synchronize()
+        ref = P.oracle_for(logits, tgt, reduction="sum")
+        P.assert_grad_close(out["grad"], ref["grad"], f"subnormal {dt}")
+        if dt == torch.float32:
+            g = out["grad"].cpu().double().numpy()
+            err = np.abs(g - ref["grad"]) - 1e-5 * np.abs(ref["grad"])
+            assert err.max() <= 2.0 ** -149, "fp32 subnormal gradients"
+            assert (g[:, 1:300] > 0).all(), "subnormal gradients flushed to zero"
+
+
+def test_api_errors_raise():
+    logits = torch.randn((4, 10), device=DEV)
+    target = torch.zeros(4, dtype=torch.int64, device=DEV)
+    with pytest.raises(vce.CEError):
+        vce.fused_fwd_bwd(logits, target, label_smoothing=1.0)
+    with pytest.raises(vce.CEError):
+        vce.fused_fwd_bwd(logits, target, grad=logits)   # grad aliases logits

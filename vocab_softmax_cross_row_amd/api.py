@@ -1,0 +1,168 @@
+"""torch-facing helpers over the C ABI: allocate outputs with torch, call
+the library, return tensors.  No arithmetic happens here; options are
+keyword-only (Megatron-core unfused_cross_entropy passes the process group
+by keyword because the third positional argument is label_smoothing).
+"""
+import torch
+
+from . import _binding as B
+
+
+def _logits2d(logits):
+    if logits.dim() != 2:
+        raise ValueError("logits must be 2-D [T, V] (flatten [seq, batch, V] first)")
+    if logits.stride(1) != 1:
+        raise ValueError("logits rows must be contiguous (stride(1) == 1)")
+    if not logits.is_cuda:
+        raise ValueError("logits must be on the GPU")
+    return logits.shape[0], logits.shape[1], (logits.stride(0) if logits.shape[0] > 1
+                                              else logits.shape[1])
+
+
+def _target(target, T):
+    if target.dtype != torch.int64 or target.dim() != 1 or target.shape[0] != T:
+        raise ValueError("target must be int64 [T]")
+    if not target.is_contiguous():
+        raise ValueError("target must be contiguous")
+    return target
+
+
+def _grad_output(grad_output, reduction, T, device):
+    if grad_output is None:
+        return None
+    if not isinstance(grad_output, torch.Tensor):
+        grad_output = torch.tensor([float(grad_output)], device=device)
+    go = grad_output.to(device=device, dtype=torch.float32).contiguous().reshape(-1)
+    need = T if reduction == "none" else 1
+    if go.numel() != need:
+        raise ValueError(f"grad_output must have {need} element(s) for reduction={reduction}")
+    return go
+
+
+def _workspace(prob, op, device):
+    n = B.ce_workspace_bytes(prob, op)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device), n
+
+
+def fused_fwd_bwd(logits, target, *, ignore_index=-100, label_smoothing=0.0, reduction="mean",
+                  grad_output=None, grad_dtype=None, grad=None, stream=None):
+    """Loss, per-row loss, counts and d loss / d logits in one call."""
+    T, V, ld = _logits2d(logits)
+    target = _target(target, T)
+    dev = logits.device
+    gdt = grad_dtype or logits.dtype
+    if grad is None:
+        grad = torch.empty((T, V), dtype=gdt, device=dev)
+    ldg = grad.stride(0) if T > 1 else V
+    prob = B.make_problem(T, V, ld, ignore_index=ignore_index, label_smoothing=label_smoothing,
+                          reduction=reduction)
+    ws, nws = _workspace(prob, B.CE_OP_FUSED, dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    loss_rows = torch.empty(T, dtype=torch.float32, device=dev)
+    n_valid = torch.empty(1, dtype=torch.int32, device=dev)
+    err = torch.empty(1, dtype=torch.int32, device=dev)
+    go = _grad_output(grad_output, reduction, T, dev)
+    B.ce_fused_fwd_bwd(prob, logits, B.dtype_code(logits.dtype), target, go, loss_rows, loss,
+                       n_valid, err, grad, B.dtype_code(gdt), ldg, ws, nws, stream)
+    return {"loss": loss, "loss_rows": loss_rows, "grad": grad, "n_valid": n_valid,
+            "err_count": err}
+
+
+def forward(logits, target, *, vocab_start=0, V_total=None, ignore_index=-100,
+            label_smoothing=0.0, reduction="mean", stream=None):
+    """Row statistics of this call's columns; when they are the whole
+    vocabulary, also the finalize (fin, per-row and reduced loss, counts)."""
+    T, V, ld = _logits2d(logits)
+    target = _target(target, T)
+    dev = logits.device
+    V_total = V if V_total is None else V_total
+    prob = B.make_problem(T, V, ld, vocab_start=vocab_start, V_total=V_total,
+                          ignore_index=ignore_index, label_smoothing=label_smoothing,
+                          reduction=reduction)
+    ws, nws = _workspace(prob, B.CE_OP_FORWARD, dev)
+    stats = torch.empty((T, B.ROW_STATS_BYTES), dtype=torch.uint8, device=dev)
+    whole = vocab_start == 0 and V == V_total
+    out = {"stats": stats}
+    fin = loss_rows = loss = n_valid = err = None
+    if whole:
+        fin = torch.empty((T, B.ROW_FINAL_BYTES), dtype=torch.uint8, device=dev)
+        loss_rows = torch.empty(T, dtype=torch.float32, device=dev)
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+        n_valid = torch.empty(1, dtype=torch.int32, device=dev)
+        err = torch.empty(1, dtype=torch.int32, device=dev)
+        out.update(fin=fin, loss_rows=loss_rows, loss=loss, n_valid=n_valid, err_count=err)
+    B.ce_forward(prob, logits, B.dtype_code(logits.dtype), target, stats, fin, loss_rows, loss,
+                 n_valid, err, ws, nws, stream)
+    return out
+
+
+def merge_shard_stats(shard_stats, target, V_total, *, ignore_index=-100, label_smoothing=0.0,
+                      reduction="mean", stream=None):
+    """Merge per-shard statistics (a list of [T, 24] buffers in shard order,
+    or one [S, T, 24] buffer) and finalize."""
+    if isinstance(shard_stats, (list, tuple)):
+        shard_stats = torch.stack(list(shard_stats))
+    S, T = shard_stats.shape[0], shard_stats.shape[1]
+    target = _target(target, T)
+    dev = target.device
+    prob = B.make_problem(T, 1, 1, V_total=V_total, ignore_index=ignore_index,
+                          label_smoothing=label_smoothing, reduction=reduction)
+    ws, nws = _workspace(prob, B.CE_OP_MERGE, dev)
+    fin = torch.empty((T, B.ROW_FINAL_BYTES), dtype=torch.uint8, device=dev)
+    loss_rows = torch.empty(T, dtype=torch.float32, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    n_valid = torch.empty(1, dtype=torch.int32, device=dev)
+    err = torch.empty(1, dtype=torch.int32, device=dev)
+    B.ce_merge_shard_stats(prob, S, shard_stats.contiguous(), target, fin, loss_rows, loss,
+                           n_valid, err, ws, nws, stream)
+    return {"fin": fin, "loss_rows": loss_rows, "loss": loss, "n_valid": n_valid,
+            "err_count": err}
+
+
+def backward(logits, target, fin, n_valid, *, grad_output=None, vocab_start=0, V_total=None,
+             ignore_index=-100, label_smoothing=0.0, reduction="mean", grad_dtype=None,
+             grad=None, stream=None):
+    """Gradient of this call's columns from the row constants `fin`."""
+    T, V, ld = _logits2d(logits)
+    target = _target(target, T)
+    dev = logits.device
+    V_total = V if V_total is None else V_total
+    gdt = grad_dtype or logits.dtype
+    if grad is None:
+        grad = torch.empty((T, V), dtype=gdt, device=dev)
+    ldg = grad.stride(0) if T > 1 else V
+    prob = B.make_problem(T, V, ld, vocab_start=vocab_start, V_total=V_total,
+                          ignore_index=ignore_index, label_smoothing=label_smoothing,
+                          reduction=reduction)
+    go = _grad_output(grad_output, reduction, T, dev)
+    B.ce_backward(prob, logits, B.dtype_code(logits.dtype), target, fin, n_valid, go, grad,
+                  B.dtype_code(gdt), ldg, stream)
+    return grad
+
+
+class CrossEntropy(torch.autograd.Function):
+    """Autograd wrapper: the forward saves the logits (never copied or
+    upcast), the targets and the 24-byte row constants; the backward runs
+    the library's gradient pass."""
+
+    @staticmethod
+    def forward(ctx, logits, target, ignore_index, label_smoothing, reduction):
+        out = forward(logits, target, ignore_index=ignore_index,
+                      label_smoothing=label_smoothing, reduction=reduction)
+        ctx.save_for_backward(logits, target, out["fin"], out["n_valid"])
+        ctx.opts = (ignore_index, label_smoothing, reduction)
+        return out["loss"][0] if reduction != "none" else out["loss_rows"]
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        logits, target, fin, n_valid = ctx.saved_tensors
+        ignore_index, label_smoothing, reduction = ctx.opts
+        g = backward(logits, target, fin, n_valid, grad_output=grad_out.reshape(-1),
+                     ignore_index=ignore_index, label_smoothing=label_smoothing,
+                     reduction=reduction)
+        return g, None, None, None, None
+
+
+def cross_entropy(logits, target, *, ignore_index=-100, label_smoothing=0.0, reduction="mean"):
+    """Differentiable stable cross-entropy over [T, V] logits."""
+    return CrossEntropy.apply(logits, target, ignore_index, label_smoothing, reduction)

@@ -1,0 +1,425 @@
+// C ABI of libvocab_ce.so (declared in include/vocab_ce.h): argument checks,
+// workspace layout and the order of launches for each entry point.  No
+// allocation, no host synchronisation; everything goes on the caller's
+// stream.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "ce_launch.h"
+#include "vocab_ce.h"
+
+namespace {
+
+using namespace vce;
+
+// Split-V grid: rows shorter than this many workgroups' worth of work are
+// split into column chunks so the streaming kernels still fill the GPU.
+constexpr int64_t kTargetBlocks = 1024;
+constexpr int64_t kMinChunkCols = 4096;
+constexpr int64_t kMaxChunks = 64;
+// The fused entry point prefers the split-V grid over the row-resident
+// kernel when there are fewer rows than this and rows are long.
+constexpr int64_t kResidentMinRows = 512;
+constexpr int64_t kResidentSplitCols = 16384;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+    int nchunks;
+    int64_t chunk_cols;
+};
+
+Plan plan_chunks(int64_t T, int64_t V_local) {
+    Plan p{1, V_local};
+    if (T <= 0 || T >= kTargetBlocks) return p;
+    int64_t n = (kTargetBlocks + T - 1) / T;
+    n = std::min(n, V_local / kMinChunkCols);
+    n = std::min(n, kMaxChunks);
+    if (n <= 1) return p;
+    int64_t cc = (V_local + n - 1) / n;
+    cc = (cc + 7) / 8 * 8; // chunk starts stay 16-byte aligned for either dtype
+    p.chunk_cols = cc;
+    p.nchunks = (int)((V_local + cc - 1) / cc);
+    return p;
+}
+
+size_t elem_size(int dt) { return dt == CE_BF16 ? 2 : 4; }
+bool dtype_ok(int dt) { return dt == CE_F32 || dt == CE_BF16; }
+
+int check_problem(const ce_problem *p) {
+    if (!p) return CE_ERR_NULL;
+    if (p->reduction != CE_RED_NONE && p->reduction != CE_RED_SUM &&
+        p->reduction != CE_RED_MEAN)
+        return CE_ERR_REDUCTION;
+    if (!std::isfinite(p->label_smoothing) || p->label_smoothing < 0.0f ||
+        p->label_smoothing >= 1.0f)
+        return CE_ERR_SMOOTHING;
+    if (p->T < 0 || p->V_local < 1 || p->ld < p->V_local || p->vocab_start < 0 ||
+        p->V_total < 1 || p->vocab_start > p->V_total - p->V_local)
+        return CE_ERR_SHAPE;
+    // grid and count limits: blocks are rows x chunks, counts are int32
+    if (p->T > (int64_t)INT32_MAX / kMaxChunks || p->V_total > ((int64_t)1 << 40) ||
+        p->ld > ((int64_t)1 << 40))
+        return CE_ERR_SHAPE;
+    return CE_OK;
+}
+
+bool aligned(const void *p, int64_t ld_bytes, size_t a) {
+    return (reinterpret_cast<uintptr_t>(p) % a) == 0 && (ld_bytes % (int64_t)a) == 0;
+}
+
+// logits rows 16-byte aligned and gradient rows aligned to one vector store
+bool vec_ok(const void *logits, int64_t ld, int in_dt, const void *grad, int64_t ldg,
+            int out_dt) {
+    if (!aligned(logits, ld * (int64_t)elem_size(in_dt), 16)) return false;
+    if (!grad) return true;
+    const size_t epv = in_dt == CE_BF16 ? 8 : 4;
+    const size_t a = std::min<size_t>(16, epv * elem_size(out_dt));
+    return aligned(grad, ldg * (int64_t)elem_size(out_dt), a);
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+size_t matrix_bytes(int64_t T, int64_t cols, int64_t ld, size_t esz) {
+    return T <= 0 ? 0 : ((size_t)(T - 1) * (size_t)ld + (size_t)cols) * esz;
+}
+
+// Workspace layout of an entry point.
+struct Layout {
+    size_t partial;   // [nchunks][T] ce_row_stats
+    size_t fin;       // [T] ce_row_final
+    size_t loss_rows; // [T] float
+    size_t n_valid;   // [1] int32
+    size_t total;
+};
+
+Layout layout(const ce_problem *p, int op) {
+    Layout l{0, 0, 0, 0, 0};
+    const int64_t T = std::max<int64_t>(p->T, 0);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align_up(bytes);
+        return o;
+    };
+    const Plan pl = plan_chunks(T, p->V_local);
+    if (op == CE_OP_FORWARD) {
+        l.partial = take(pl.nchunks > 1 ? (size_t)pl.nchunks * T * sizeof(ce_row_stats) : 0);
+        l.loss_rows = take((size_t)T * sizeof(float));
+        l.n_valid = take(sizeof(int32_t));
+    } else if (op == CE_OP_FUSED) {
+        l.partial = take((size_t)std::max(pl.nchunks, 1) * T * sizeof(ce_row_stats));
+        l.fin = take((size_t)T * sizeof(ce_row_final));
+        l.loss_rows = take((size_t)T * sizeof(float));
+        l.n_valid = take(sizeof(int32_t));
+    } else if (op == CE_OP_MERGE) {
+        l.loss_rows = take((size_t)T * sizeof(float));
+        l.n_valid = take(sizeof(int32_t));
+    }
+    l.total = off;
+    return l;
+}
+
+int check_ws(const ce_problem *p, int op, void *ws, size_t ws_bytes, Layout *l) {
+    *l = layout(p, op);
+    if (l->total == 0) return CE_OK;
+    if (!ws || ws_bytes < l->total || reinterpret_cast<uintptr_t>(ws) % 16 != 0)
+        return CE_ERR_WORKSPACE;
+    return CE_OK;
+}
+
+template <class T>
+T *at(void *ws, size_t off) {
+    return reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+
+#define VCE_TRY(expr)                                                                            \
+    do {                                                                                         \
+        const hipError_t e_ = (expr);                                                            \
+        if (e_ != hipSuccess) return CE_ERR_HIP;                                                 \
+    } while (0)
+
+} // namespace
+
+extern "C" {
+
+size_t ce_workspace_bytes(const ce_problem *prob, int op) {
+    if (check_problem(prob) != CE_OK) return 0;
+    if (op != CE_OP_FORWARD && op != CE_OP_BACKWARD && op != CE_OP_FUSED && op != CE_OP_MERGE)
+        return 0;
+    return layout(prob, op).total;
+}
+
+int ce_forward(const ce_problem *prob, const void *logits, int logits_dtype,
+               const int64_t *target, ce_row_stats *stats, ce_row_final *fin, float *loss_rows,
+               float *loss, int32_t *n_valid, int32_t *err_count, void *ws, size_t ws_bytes,
+               void *stream) {
+    int rc = check_problem(prob);
+    if (rc != CE_OK) return rc;
+    if (!dtype_ok(logits_dtype)) return CE_ERR_DTYPE;
+    const ce_problem &p = *prob;
+    const bool whole = p.vocab_start == 0 && p.V_local == p.V_total;
+    if (!whole && (fin || loss_rows || loss || n_valid || err_count)) return CE_ERR_ARG;
+    if (p.T > 0 && (!logits || !target || !stats)) return CE_ERR_NULL;
+    Layout l;
+    if ((rc = check_ws(prob, CE_OP_FORWARD, ws, ws_bytes, &l)) != CE_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    if (whole) {
+        int32_t *nv = n_valid ? n_valid : at<int32_t>(ws, l.n_valid);
+        VCE_TRY(launch_count(target, p.T, p.ignore_index, p.V_total, nv, err_count, s));
+        if (p.T == 0) {
+            if (loss && p.reduction != CE_RED_NONE)
+                VCE_TRY(launch_reduce(nullptr, 0, p.reduction, nv, loss, s));
+            return CE_OK;
+        }
+    } else if (p.T == 0) {
+        return CE_OK;
+    }
+
+    const Plan pl = plan_chunks(p.T, p.V_local);
+    StatsArgs sa;
+    sa.logits = logits;
+    sa.ld = p.ld;
+    sa.V_local = p.V_local;
+    sa.vocab_start = p.vocab_start;
+    sa.V_total = p.V_total;
+    sa.target = target;
+    sa.ignore_index = p.ignore_index;
+    sa.T = p.T;
+    sa.nchunks = pl.nchunks;
+    sa.chunk_cols = pl.chunk_cols;
+    sa.out = pl.nchunks > 1 ? at<ce_row_stats>(ws, l.partial) : stats;
+    sa.smoothing = p.label_smoothing > 0.0f;
+    const bool vec = vec_ok(logits, p.ld, logits_dtype, nullptr, 0, CE_F32);
+    VCE_TRY(launch_stats(sa, logits_dtype, vec, s));
+
+    MergeArgs ma;
+    ma.T = p.T;
+    ma.target = target;
+    ma.ignore_index = p.ignore_index;
+    ma.V_total = p.V_total;
+    ma.eps = p.label_smoothing;
+    if (pl.nchunks > 1) {
+        // column chunks -> this call's statistics (and the finalize if whole)
+        ma.in = sa.out;
+        ma.S = pl.nchunks;
+        ma.stats_out = stats;
+    } else {
+        ma.in = stats;
+        ma.S = 1;
+        ma.stats_out = nullptr;
+    }
+    ma.fin = whole ? fin : nullptr;
+    float *lr = loss_rows ? loss_rows : at<float>(ws, l.loss_rows);
+    ma.loss_rows = whole ? lr : nullptr;
+    if (ma.stats_out || ma.fin || ma.loss_rows) VCE_TRY(launch_merge(ma, s));
+
+    if (whole && loss && p.reduction != CE_RED_NONE) {
+        const int32_t *nv = n_valid ? n_valid : at<int32_t>(ws, l.n_valid);
+        VCE_TRY(launch_reduce(lr, p.T, p.reduction, nv, loss, s));
+    }
+    return CE_OK;
+}
+
+int ce_merge_shard_stats(const ce_problem *prob, int n_shards, const ce_row_stats *shard_stats,
+                         const int64_t *target, ce_row_final *fin, float *loss_rows, float *loss,
+                         int32_t *n_valid, int32_t *err_count, void *ws, size_t ws_bytes,
+                         void *stream) {
+    int rc = check_problem(prob);
+    if (rc != CE_OK) return rc;
+    if (n_shards < 1 || n_shards > CE_MAX_SHARDS) return CE_ERR_SHARDS;
+    const ce_problem &p = *prob;
+    if (p.T > 0 && (!shard_stats || !target || !fin)) return CE_ERR_NULL;
+    Layout l;
+    if ((rc = check_ws(prob, CE_OP_MERGE, ws, ws_bytes, &l)) != CE_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    int32_t *nv = n_valid ? n_valid : at<int32_t>(ws, l.n_valid);
+    VCE_TRY(launch_count(target, p.T, p.ignore_index, p.V_total, nv, err_count, s));
+    float *lr = loss_rows ? loss_rows : at<float>(ws, l.loss_rows);
+    if (p.T > 0) {
+        MergeArgs ma;
+        ma.in = shard_stats;
+        ma.S = n_shards;
+        ma.T = p.T;
+        ma.target = target;
+        ma.ignore_index = p.ignore_index;
+        ma.V_total = p.V_total;
+        ma.eps = p.label_smoothing;
+        ma.stats_out = nullptr;
+        ma.fin = fin;
+        ma.loss_rows = lr;
+        VCE_TRY(launch_merge(ma, s));
+    }
+    if (loss && p.reduction != CE_RED_NONE)
+        VCE_TRY(launch_reduce(lr, p.T, p.reduction, nv, loss, s));
+    return CE_OK;
+}
+
+int ce_backward(const ce_problem *prob, const void *logits, int logits_dtype,
+                const int64_t *target, const ce_row_final *fin, const int32_t *n_valid,
+                const float *grad_output, void *grad, int grad_dtype, int64_t ldg,
+                void *stream) {
+    int rc = check_problem(prob);
+    if (rc != CE_OK) return rc;
+    if (!dtype_ok(logits_dtype) || !dtype_ok(grad_dtype)) return CE_ERR_DTYPE;
+    const ce_problem &p = *prob;
+    if (ldg < p.V_local) return CE_ERR_SHAPE;
+    if (p.T == 0) return CE_OK;
+    if (!logits || !target || !fin || !grad) return CE_ERR_NULL;
+    if (p.reduction == CE_RED_MEAN && !n_valid) return CE_ERR_NULL;
+    if (overlaps(logits, matrix_bytes(p.T, p.V_local, p.ld, elem_size(logits_dtype)), grad,
+                 matrix_bytes(p.T, p.V_local, ldg, elem_size(grad_dtype))))
+        return CE_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    const Plan pl = plan_chunks(p.T, p.V_local);
+    GradArgs ga;
+    ga.logits = logits;
+    ga.ld = p.ld;
+    ga.V_local = p.V_local;
+    ga.vocab_start = p.vocab_start;
+    ga.V_total = p.V_total;
+    ga.target = target;
+    ga.fin = fin;
+    ga.n_valid = n_valid;
+    ga.grad_output = grad_output;
+    ga.reduction = p.reduction;
+    ga.eps = p.label_smoothing;
+    ga.grad = grad;
+    ga.ldg = ldg;
+    ga.nchunks = pl.nchunks;
+    ga.chunk_cols = pl.chunk_cols;
+    const bool vec = vec_ok(logits, p.ld, logits_dtype, grad, ldg, grad_dtype);
+    VCE_TRY(launch_grad(ga, logits_dtype, grad_dtype, vec, p.T, s));
+    return CE_OK;
+}
+
+int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtype,
+                     const int64_t *target, const float *grad_output, float *loss_rows,
+                     float *loss, int32_t *n_valid, int32_t *err_count, void *grad,
+                     int grad_dtype, int64_t ldg, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_problem(prob);
+    if (rc != CE_OK) return rc;
+    if (!dtype_ok(logits_dtype) || !dtype_ok(grad_dtype)) return CE_ERR_DTYPE;
+    const ce_problem &p = *prob;
+    if (p.vocab_start != 0 || p.V_local != p.V_total) return CE_ERR_ARG;
+    if (ldg < p.V_local) return CE_ERR_SHAPE;
+    if (p.T > 0 && (!logits || !target || !grad)) return CE_ERR_NULL;
+    Layout l;
+    if ((rc = check_ws(prob, CE_OP_FUSED, ws, ws_bytes, &l)) != CE_OK) return rc;
+    if (p.T > 0 &&
+        overlaps(logits, matrix_bytes(p.T, p.V_local, p.ld, elem_size(logits_dtype)), grad,
+                 matrix_bytes(p.T, p.V_local, ldg, elem_size(grad_dtype))))
+        return CE_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+
+    int32_t *nv = n_valid ? n_valid : at<int32_t>(ws, l.n_valid);
+    VCE_TRY(launch_count(target, p.T, p.ignore_index, p.V_total, nv, err_count, s));
+    float *lr = loss_rows ? loss_rows : at<float>(ws, l.loss_rows);
+
+    if (p.T > 0) {
+        const bool vec = vec_ok(logits, p.ld, logits_dtype, grad, ldg, grad_dtype);
+        const bool split = p.T < kResidentMinRows && p.V_local >= kResidentSplitCols;
+        if (vec && !split && resident_threads(logits_dtype, p.V_local) > 0) {
+            FusedArgs fa;
+            fa.logits = logits;
+            fa.ld = p.ld;
+            fa.V = p.V_local;
+            fa.target = target;
+            fa.ignore_index = p.ignore_index;
+            fa.grad = grad;
+            fa.ldg = ldg;
+            fa.grad_output = grad_output;
+            fa.n_valid = nv;
+            fa.loss_rows = lr;
+            fa.reduction = p.reduction;
+            fa.eps = p.label_smoothing;
+            VCE_TRY(launch_fused_resident(fa, logits_dtype, grad_dtype, p.T, s));
+        } else {
+            // streaming: stats (column chunks) -> merge + finalize -> gradient
+            const Plan pl = plan_chunks(p.T, p.V_local);
+            StatsArgs sa;
+            sa.logits = logits;
+            sa.ld = p.ld;
+            sa.V_local = p.V_local;
+            sa.vocab_start = 0;
+            sa.V_total = p.V_total;
+            sa.target = target;
+            sa.ignore_index = p.ignore_index;
+            sa.T = p.T;
+            sa.nchunks = pl.nchunks;
+            sa.chunk_cols = pl.chunk_cols;
+            sa.out = at<ce_row_stats>(ws, l.partial);
+            sa.smoothing = p.label_smoothing > 0.0f;
+            VCE_TRY(launch_stats(sa, logits_dtype, vec, s));
+
+            ce_row_final *fin = at<ce_row_final>(ws, l.fin);
+            MergeArgs ma;
+            ma.in = sa.out;
+            ma.S = pl.nchunks;
+            ma.T = p.T;
+            ma.target = target;
+            ma.ignore_index = p.ignore_index;
+            ma.V_total = p.V_total;
+            ma.eps = p.label_smoothing;
+            ma.stats_out = nullptr;
+            ma.fin = fin;
+            ma.loss_rows = lr;
+            VCE_TRY(launch_merge(ma, s));
+
+            GradArgs ga;
+            ga.logits = logits;
+            ga.ld = p.ld;
+            ga.V_local = p.V_local;
+            ga.vocab_start = 0;
+            ga.V_total = p.V_total;
+            ga.target = target;
+            ga.fin = fin;
+            ga.n_valid = nv;
+            ga.grad_output = grad_output;
+            ga.reduction = p.reduction;
+            ga.eps = p.label_smoothing;
+            ga.grad = grad;
+            ga.ldg = ldg;
+            ga.nchunks = pl.nchunks;
+            ga.chunk_cols = pl.chunk_cols;
+            VCE_TRY(launch_grad(ga, logits_dtype, grad_dtype, vec, p.T, s));
+        }
+    }
+    if (loss && p.reduction != CE_RED_NONE)
+        VCE_TRY(launch_reduce(lr, p.T, p.reduction, nv, loss, s));
+    return CE_OK;
+}
+
+const char *ce_status_str(int status) {
+    switch (status) {
+    case CE_OK: return "CE_OK";
+    case CE_ERR_NULL: return "CE_ERR_NULL: a required pointer is NULL";
+    case CE_ERR_SHAPE: return "CE_ERR_SHAPE: invalid or too large shape, stride or vocabulary range";
+    case CE_ERR_SMOOTHING: return "CE_ERR_SMOOTHING: label_smoothing must be finite and in [0, 1)";
+    case CE_ERR_DTYPE: return "CE_ERR_DTYPE: unknown dtype";
+    case CE_ERR_REDUCTION: return "CE_ERR_REDUCTION: unknown reduction";
+    case CE_ERR_WORKSPACE: return "CE_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case CE_ERR_SHARDS: return "CE_ERR_SHARDS: n_shards out of range";
+    case CE_ERR_ALIAS: return "CE_ERR_ALIAS: grad overlaps logits";
+    case CE_ERR_HIP: return "CE_ERR_HIP: a HIP launch failed";
+    case CE_ERR_ARG: return "CE_ERR_ARG: output requested that this call cannot produce";
+    default: return "unknown ce_status";
+    }
+}
+
+int ce_version(void) { return 100; }
+
+} // extern "C"

@@ -1,0 +1,430 @@
+// Device-side building blocks of the cross-entropy kernels for gfx950
+// (CDNA4, wave64): element access for bf16 / fp32 logits held in 16-byte
+// vectors, stores of bf16 / fp32 gradients, wave and workgroup reductions,
+// and the per-row fp64 finalize.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "vocab_ce.h"
+
+namespace vce {
+
+// log2(e) rounded to binary32 (0x3FB8AA3B).  Every exponential below is
+// 2^(z * kL2E - K): the per-row constant K absorbs how kL2E differs from
+// log2(e) at the row's reference point, so only (z - ref) * (kL2E - log2 e)
+// is left, below 2e-8 per unit of distance.
+constexpr float kL2E = 1.44269502162933349609375f;
+constexpr double kL2E_d = 1.44269502162933349609375;     // the same value, exactly
+constexpr double kLog2e = 1.442695040888963407359924681; // log2(e)
+// log2(e) - kL2E, the low half of a two-float log2(e)
+constexpr float kL2E_lo = (float)(kLog2e - kL2E_d);
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float ninf() { return -__builtin_inff(); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+struct alignas(16) U4 {
+    uint32_t w[4];
+};
+
+// ---------------------------------------------------------------------------
+// A group of EPV consecutive logits of one row, kept in their storage format.
+// ---------------------------------------------------------------------------
+template <int DT, int EPV>
+struct Chunk;
+
+template <>
+struct Chunk<CE_BF16, 8> {
+    static constexpr int kBytes = 16;
+    U4 v;
+    __device__ __forceinline__ void load(const void *p) { v = *static_cast<const U4 *>(p); }
+    __device__ __forceinline__ void fill_ninf() { v.w[0] = v.w[1] = v.w[2] = v.w[3] = 0xff80ff80u; }
+    __device__ __forceinline__ float get(int e) const {
+        const uint32_t x = v.w[e >> 1];
+        return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
+    }
+    // e may be a run-time value: every word is visited with a select, so the
+    // vector never has to leave registers
+    __device__ __forceinline__ void kill(int e) {
+        const uint32_t keep = (e & 1) ? 0x0000ffffu : 0xffff0000u;
+        const uint32_t put = (e & 1) ? 0xff800000u : 0x0000ff80u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v.w[k] = (k == (e >> 1)) ? ((v.w[k] & keep) | put) : v.w[k];
+    }
+};
+
+template <>
+struct Chunk<CE_F32, 4> {
+    static constexpr int kBytes = 16;
+    U4 v;
+    __device__ __forceinline__ void load(const void *p) { v = *static_cast<const U4 *>(p); }
+    __device__ __forceinline__ void fill_ninf() { v.w[0] = v.w[1] = v.w[2] = v.w[3] = 0xff800000u; }
+    __device__ __forceinline__ float get(int e) const { return __uint_as_float(v.w[e]); }
+    __device__ __forceinline__ void kill(int e) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v.w[k] = (k == e) ? 0xff800000u : v.w[k];
+    }
+};
+
+template <>
+struct Chunk<CE_BF16, 1> {
+    static constexpr int kBytes = 2;
+    uint32_t v;
+    __device__ __forceinline__ void load(const void *p) {
+        v = (uint32_t)(*static_cast<const uint16_t *>(p)) << 16;
+    }
+    __device__ __forceinline__ void fill_ninf() { v = 0xff800000u; }
+    __device__ __forceinline__ float get(int) const { return __uint_as_float(v); }
+    __device__ __forceinline__ void kill(int) { v = 0xff800000u; }
+};
+
+template <>
+struct Chunk<CE_F32, 1> {
+    static constexpr int kBytes = 4;
+    uint32_t v;
+    __device__ __forceinline__ void load(const void *p) { v = *static_cast<const uint32_t *>(p); }
+    __device__ __forceinline__ void fill_ninf() { v = 0xff800000u; }
+    __device__ __forceinline__ float get(int) const { return __uint_as_float(v); }
+    __device__ __forceinline__ void kill(int) { v = 0xff800000u; }
+};
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<CE_BF16> {
+    static constexpr int kSize = 2;
+    static constexpr int kVec = 8; // elements per 16-byte vector
+    __device__ __forceinline__ static float load1(const void *p) {
+        return __uint_as_float((uint32_t)(*static_cast<const uint16_t *>(p)) << 16);
+    }
+};
+template <>
+struct Elem<CE_F32> {
+    static constexpr int kSize = 4;
+    static constexpr int kVec = 4;
+    __device__ __forceinline__ static float load1(const void *p) {
+        return *static_cast<const float *>(p);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Gradient stores: N consecutive values, the address aligned to N elements
+// (N * size bytes, capped at 16).
+// ---------------------------------------------------------------------------
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    f32x2_t f = {lo, hi};
+    bf16x2_t b = __builtin_convertvector(f, bf16x2_t); // v_cvt_pk_bf16_f32: RNE
+    return __builtin_bit_cast(uint32_t, b);
+}
+
+template <int DT, int N>
+struct Store;
+
+template <int N>
+struct Store<CE_BF16, N> {
+    __device__ __forceinline__ static void put(void *p, const float *g) {
+        if constexpr (N == 8) {
+            U4 o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o.w[i] = pack_bf16x2(g[2 * i], g[2 * i + 1]);
+            *static_cast<U4 *>(p) = o;
+        } else if constexpr (N == 4) {
+            uint2 o;
+            o.x = pack_bf16x2(g[0], g[1]);
+            o.y = pack_bf16x2(g[2], g[3]);
+            *static_cast<uint2 *>(p) = o;
+        } else {
+            static_assert(N == 1, "unsupported width");
+            *static_cast<uint16_t *>(p) = (uint16_t)(pack_bf16x2(g[0], 0.0f) & 0xffffu);
+        }
+    }
+};
+
+template <int N>
+struct Store<CE_F32, N> {
+    __device__ __forceinline__ static void put(void *p, const float *g) {
+        if constexpr (N == 8) {
+            U4 a, b;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a.w[i] = __float_as_uint(g[i]);
+                b.w[i] = __float_as_uint(g[4 + i]);
+            }
+            static_cast<U4 *>(p)[0] = a;
+            static_cast<U4 *>(p)[1] = b;
+        } else if constexpr (N == 4) {
+            U4 a;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a.w[i] = __float_as_uint(g[i]);
+            *static_cast<U4 *>(p) = a;
+        } else {
+            static_assert(N == 1, "unsupported width");
+            *static_cast<float *>(p) = g[0];
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Reductions.  Fixed butterfly inside a wave, then wave partials combined in
+// wave order by every thread: deterministic run to run.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+// (max, sum) pair: s = sum of exp(z - m) over the values seen so far, in
+// fp64.  Combining two pairs rescales the side with the smaller max.
+struct MaxSum {
+    float m;
+    double s;
+};
+__device__ __forceinline__ MaxSum combine(MaxSum a, MaxSum b) {
+    const float M = fmaxf(a.m, b.m);
+    if (M == ninf()) return {M, 0.0};
+    const double sa = (a.m == ninf()) ? 0.0 : a.s * exp((double)a.m - (double)M);
+    const double sb = (b.m == ninf()) ? 0.0 : b.s * exp((double)b.m - (double)M);
+    return {M, sa + sb};
+}
+__device__ __forceinline__ MaxSum wave_combine(MaxSum v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        MaxSum w = {__shfl_xor(v.m, o, kWave), __shfl_xor(v.s, o, kWave)};
+        // both lanes of a pair compute the same result in the same order
+        const bool lower = (threadIdx.x & o) == 0;
+        v = lower ? combine(v, w) : combine(w, v);
+    }
+    return v;
+}
+
+template <int THREADS>
+struct BlockRed {
+    static constexpr int kWaves = THREADS / kWave;
+    static_assert(THREADS % kWave == 0, "THREADS must be a multiple of 64");
+    float f[2][kWaves];
+    double d[2][kWaves];
+};
+
+// Workgroup-wide max; every thread returns the result.  `red` is shared.
+template <int THREADS>
+__device__ __forceinline__ float block_max(float v, BlockRed<THREADS> &red, int slot) {
+    v = wave_max(v);
+    const int wv = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) red.f[slot][wv] = v;
+    __syncthreads();
+    float r = red.f[slot][0];
+#pragma unroll
+    for (int i = 1; i < BlockRed<THREADS>::kWaves; ++i) r = fmaxf(r, red.f[slot][i]);
+    return r;
+}
+
+template <int THREADS>
+__device__ __forceinline__ float block_sum(float v, BlockRed<THREADS> &red, int slot) {
+    v = wave_sum(v);
+    const int wv = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) red.f[slot][wv] = v;
+    __syncthreads();
+    float r = red.f[slot][0];
+#pragma unroll
+    for (int i = 1; i < BlockRed<THREADS>::kWaves; ++i) r += red.f[slot][i];
+    return r;
+}
+
+template <int THREADS>
+__device__ __forceinline__ double block_sum_d(double v, BlockRed<THREADS> &red, int slot) {
+    v = wave_sum(v);
+    const int wv = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) red.d[slot][wv] = v;
+    __syncthreads();
+    double r = red.d[slot][0];
+#pragma unroll
+    for (int i = 1; i < BlockRed<THREADS>::kWaves; ++i) r += red.d[slot][i];
+    return r;
+}
+
+template <int THREADS>
+__device__ __forceinline__ MaxSum block_combine(MaxSum v, BlockRed<THREADS> &red) {
+    v = wave_combine(v);
+    const int wv = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        red.f[0][wv] = v.m;
+        red.d[0][wv] = v.s;
+    }
+    __syncthreads();
+    MaxSum r = {red.f[0][0], red.d[0][0]};
+#pragma unroll
+    for (int i = 1; i < BlockRed<THREADS>::kWaves; ++i) r = combine(r, {red.f[0][i], red.d[0][i]});
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Per-row finalize in fp64 (torchtitan PR "[loss] fix softmax collapse with
+// improved ce perf", Numerics; label smoothing uniform over the V classes).
+// ---------------------------------------------------------------------------
+struct RowFinal {
+    double x, nll, lse, gt, loss;
+};
+
+__device__ __forceinline__ double softplus_d(double x) {
+    if (x == -__builtin_inf()) return 0.0;
+    if (x == __builtin_inf()) return x;
+    return fmax(x, 0.0) + log1p(exp(-fabs(x)));
+}
+
+// m: non-target max; s: sum of exp(z_j - m) over non-targets; zt: target
+// logit; sz: sum of the whole row; V: vocabulary size; eps: smoothing.
+__device__ inline RowFinal finalize_row(double m, double s, double zt, double sz, double V,
+                                        double eps) {
+    RowFinal f;
+    const double inf = __builtin_inf();
+    if (s == 0.0)
+        f.x = (zt == -inf) ? __builtin_nan("") : -inf;
+    else if (zt == -inf)
+        f.x = inf;
+    else
+        f.x = (m - zt) + log(s);
+    f.nll = softplus_d(f.x);
+    if (zt == -inf)
+        f.lse = (s == 0.0) ? __builtin_nan("") : m + log(s);
+    else
+        f.lse = zt + f.nll;
+    // target select: p_t - 1 while p_t < 1/4, else minus the non-target
+    // probability, each a single exponential and divide
+    const double pt = 1.0 / (1.0 + exp(f.x));
+    const double gt = (pt < 0.25) ? pt - 1.0 : -1.0 / (1.0 + exp(-f.x));
+    f.gt = gt + eps * (V - 1.0) / V;
+    f.loss = (eps == 0.0) ? f.nll : (1.0 - eps) * f.nll + eps * (f.lse - sz / V);
+    return f;
+}
+
+// Scale k_r of a row's gradient.
+__device__ __forceinline__ double row_scale(int reduction, const float *grad_output,
+                                            const int32_t *n_valid, int64_t row) {
+    double g = 1.0;
+    if (reduction == CE_RED_NONE) {
+        if (grad_output) g = (double)grad_output[row];
+        return g;
+    }
+    if (grad_output) g = (double)grad_output[0];
+    if (reduction == CE_RED_MEAN) g /= (double)n_valid[0];
+    return g;
+}
+
+// Per-row constants of the gradient pass (fp32, what the element loop uses).
+// p_j = exp(z_j - lse) is evaluated as 2^(z_j * kL2E - C) with
+// C = lse * kL2E (so the fp32 log2(e) costs only (z_j - lse)(kL2E - log2 e)).
+//   fast  (bf16 out, eps = 0):  g = 2^(z kL2E - cb) * scale, cb = C - B and
+//         scale = k 2^(cb - C): the bias B keeps 2^(.) out of the range the
+//         hardware exponential flushes, the fp32 rounding of cb is folded
+//         into scale; it costs about 3e-6 relative, far below a bf16 ulp.
+//   exact (fp32 out, or eps > 0): log2 p = (z kL2E - ch) - cl with C = ch + cl,
+//         accurate near p = 1; the exponential is range-extended so that
+//         subnormal results survive.
+//   eps > 0: g = k p - k u (u = eps / V); where p is within a factor
+//         sqrt(2) of u the difference is rebuilt from w = log2(p / u),
+//         computed with a two-float log2(e) against d2 = d2hi + d2lo, as
+//         k u expm1(w ln 2).
+//   target: g = gk.
+struct GradConst {
+    float cb, scale, ch, cl, k, gk, ku, lu, d2hi, d2lo;
+};
+
+__device__ inline GradConst grad_constants(double lse, double gt, double k, double eps,
+                                           double V) {
+    GradConst c;
+    const double C = lse * kL2E_d;
+    int B = 64;
+    const double ka = fabs(k);
+    if (ka > 0.0 && ka < __builtin_inf()) {
+        const int ek = ilogb(ka);
+        B = ek + 120;
+        B = B > 100 ? 100 : (B < 0 ? 0 : B);
+    }
+    c.cb = (float)(C - (double)B);
+    c.scale = (float)(k * exp2((double)c.cb - C));
+    c.ch = (float)C;
+    c.cl = (float)(C - (double)c.ch);
+    c.k = (float)k;
+    c.gk = (float)(k * gt);
+    c.ku = 0.0f;
+    c.lu = 0.0f;
+    c.d2hi = c.d2lo = 0.0f;
+    if (eps > 0.0) {
+        const double u = eps / V;
+        c.ku = (float)(k * u);
+        c.lu = (float)log2(u);
+        const double d2 = lse * kLog2e + log2(u);
+        c.d2hi = (float)d2;
+        c.d2lo = (float)(d2 - (double)c.d2hi);
+    }
+    return c;
+}
+
+// 2^x for any x, subnormal results included: the hardware exponential
+// flushes results below 2^-126, so such arguments are evaluated 64 higher
+// and scaled back.
+__device__ __forceinline__ float exp2_full(float x) {
+    const bool low = x < -126.0f;
+    const float y = fast_exp2(low ? x + 64.0f : x);
+    return low ? y * 0x1p-64f : y;
+}
+
+// expm1(w ln 2) for |w| <= 1/2 (Taylor series of e^y - 1 in y = w ln 2,
+// |y| <= 0.35, through y^9: truncation below 1e-10 relative).
+__device__ __forceinline__ float expm1_base2_small(float w) {
+    const float y = w * 0.693147180559945309f;
+    float p = 1.0f / 362880.0f;
+    p = fmaf(p, y, 1.0f / 40320.0f);
+    p = fmaf(p, y, 1.0f / 5040.0f);
+    p = fmaf(p, y, 1.0f / 720.0f);
+    p = fmaf(p, y, 1.0f / 120.0f);
+    p = fmaf(p, y, 1.0f / 24.0f);
+    p = fmaf(p, y, 1.0f / 6.0f);
+    p = fmaf(p, y, 0.5f);
+    p = fmaf(p, y, 1.0f);
+    return p * y;
+}
+
+// Gradient of one non-target element (see GradConst).
+template <int OUT, bool LS>
+__device__ __forceinline__ float grad_elem(float z, const GradConst &c) {
+    if constexpr (LS) {
+        const float l2p = fmaf(z, kL2E, -c.ch) - c.cl;
+        float g = fmaf(fast_exp2(l2p), c.k, -c.ku);
+        if (__builtin_expect(fabsf(l2p - c.lu) < 0.5f, 0)) {
+            const float w = fmaf(z, kL2E, -c.d2hi) + fmaf(z, kL2E_lo, -c.d2lo);
+            g = c.ku * expm1_base2_small(w);
+        }
+        return g;
+    } else if constexpr (OUT == CE_F32) {
+        return exp2_full(fmaf(z, kL2E, -c.ch) - c.cl) * c.k;
+    } else {
+        return fast_exp2(fmaf(z, kL2E, -c.cb)) * c.scale;
+    }
+}
+
+} // namespace vce

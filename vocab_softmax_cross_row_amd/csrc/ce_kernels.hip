@@ -1,0 +1,690 @@
+// Cross-entropy kernels for gfx950 and the C ABI declared in vocab_ce.h.
+//
+// Paths
+//   fused, row resident: one workgroup per row holds the whole row in
+//     registers (16-byte vectors, up to 16 per thread), so the logits are
+//     read from HBM once and the gradient written once: a max sweep, a
+//     sum-of-exponentials sweep, an fp64 finalize by one thread, then the
+//     gradient sweep, all from registers (torchtitan PR "[loss] fix softmax
+//     collapse with improved ce perf", Memory/perf: one read of the logits,
+//     the backward rebuilt in one fused pass).
+//   streaming: the stats kernel (one read, online max / sum per thread),
+//     the finalize kernel (merge of column-chunk or shard statistics, fp64
+//     finalize) and the gradient kernel (one read, one write).  They serve
+//     ce_forward / ce_merge_shard_stats / ce_backward, and the fused entry
+//     point when the row does not fit in registers, when rows are not
+//     16-byte aligned, or when there are too few rows to fill the GPU (then
+//     each row is split into column chunks: the split-V grid).
+//   count and reduce: N_valid / bad-target counts before the gradient needs
+//     them, and the deterministic loss sum.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "ce_device.h"
+#include "ce_launch.h"
+#include "vocab_ce.h"
+
+namespace vce {
+
+// ===========================================================================
+// count: N_valid and bad targets (one workgroup, any T)
+// ===========================================================================
+constexpr int kCountThreads = 1024;
+
+__global__ __launch_bounds__(kCountThreads) void k_count(const int64_t *__restrict__ target,
+                                                         int64_t T, int64_t ignore_index,
+                                                         int64_t V_total, int32_t *n_valid,
+                                                         int32_t *err_count) {
+    __shared__ BlockRed<kCountThreads> red;
+    int nv = 0, nb = 0;
+    for (int64_t r = threadIdx.x; r < T; r += kCountThreads) {
+        const int64_t t = target[r];
+        if (t == ignore_index) continue;
+        if (t >= 0 && t < V_total)
+            ++nv;
+        else
+            ++nb;
+    }
+    // two integer sums through the float slots would lose bits: use waves
+    nv = wave_sum(nv);
+    nb = wave_sum(nb);
+    __shared__ int part[2][kCountThreads / kWave];
+    const int wv = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        part[0][wv] = nv;
+        part[1][wv] = nb;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int a = 0, b = 0;
+        for (int i = 0; i < kCountThreads / kWave; ++i) {
+            a += part[0][i];
+            b += part[1][i];
+        }
+        if (n_valid) *n_valid = a;
+        if (err_count) *err_count = b;
+    }
+    (void)red;
+}
+
+// ===========================================================================
+// reduce: loss = sum of loss_rows (fp64, fixed order), / N_valid for mean
+// ===========================================================================
+constexpr int kReduceThreads = 1024;
+
+__global__ __launch_bounds__(kReduceThreads) void k_reduce(const float *__restrict__ loss_rows,
+                                                           int64_t T, int reduction,
+                                                           const int32_t *n_valid, float *loss) {
+    __shared__ BlockRed<kReduceThreads> red;
+    double acc = 0.0;
+    for (int64_t r = threadIdx.x; r < T; r += kReduceThreads) acc += (double)loss_rows[r];
+    acc = block_sum_d(acc, red, 0);
+    if (threadIdx.x == 0) {
+        if (reduction == CE_RED_MEAN) acc /= (double)(*n_valid);
+        *loss = (float)acc;
+    }
+}
+
+// ===========================================================================
+// fused, row resident
+// ===========================================================================
+
+template <int IN, int OUT, int THREADS, int NV, bool LS>
+__global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
+    using In = Elem<IN>;
+    constexpr int EPV = In::kVec;
+    using Ch = Chunk<IN, EPV>;
+    using St = Store<OUT, EPV>;
+    constexpr int kOutSize = (OUT == CE_BF16) ? 2 : 4;
+
+    __shared__ BlockRed<THREADS> red;
+    __shared__ GradConst gc_sh;
+
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid & (kWave - 1);
+    const int64_t row = blockIdx.x;
+    const int64_t V = a.V;
+    const int64_t nvec = V / EPV;
+    const int64_t tail0 = nvec * EPV;
+    const int ntail = (int)(V - tail0);
+    const char *zrow = static_cast<const char *>(a.logits) + row * a.ld * In::kSize;
+    char *grow = static_cast<char *>(a.grad) + row * a.ldg * kOutSize;
+
+    const int64_t t = a.target[row];
+    if (t == a.ignore_index || t < 0 || t >= V) {
+        // ignored row or bad target: zero gradient, no reads of the row
+        float zero[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) zero[e] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int64_t vi = (int64_t)i * THREADS + tid;
+            if (vi < nvec) St::put(grow + vi * EPV * kOutSize, zero);
+        }
+        if (tid < ntail) Store<OUT, 1>::put(grow + (tail0 + tid) * kOutSize, zero);
+        if (tid == 0) a.loss_rows[row] = (t == a.ignore_index) ? 0.0f : __builtin_nanf("");
+        return;
+    }
+
+    // ---- load the row into registers -------------------------------------
+    Ch v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int64_t vi = (int64_t)i * THREADS + tid;
+        if (vi < nvec)
+            v[i].load(zrow + vi * EPV * In::kSize);
+        else
+            v[i].fill_ninf();
+    }
+    float ztail = ninf();
+    if (tid < ntail) ztail = In::load1(zrow + (tail0 + tid) * In::kSize);
+
+    // where the target sits: vector tv (slot tv / THREADS of thread
+    // tv % THREADS) and element te, or in the scalar tail
+    const int64_t tv = t / EPV;
+    const int te = (int)(t % EPV);
+    const bool t_in_vec = t < tail0;
+    const int t_slot = (int)(tv / THREADS);
+    const int t_owner = (int)(tv % THREADS);
+
+    // ---- sum of the whole row (smoothing only), before the target is masked
+    double sz = 0.0;
+    if constexpr (LS) {
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int64_t vi = (int64_t)i * THREADS + tid;
+            float p[EPV];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) p[e] = v[i].get(e);
+#pragma unroll
+            for (int h = EPV / 2; h > 0; h >>= 1)
+#pragma unroll
+                for (int e = 0; e < h; ++e) p[e] += p[e + h];
+            sz += (vi < nvec) ? (double)p[0] : 0.0;
+        }
+        if (tid < ntail) sz += (double)ztail;
+    }
+
+    // ---- drop the target before any reduction (it sits in one lane) ------
+    if (t_in_vec) {
+        if (wave == (t_owner >> 6)) {
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                if (i == t_slot && lane == (t_owner & 63)) v[i].kill(te);
+        }
+    } else if (tid == (int)(t - tail0)) {
+        ztail = ninf();
+    }
+
+    // ---- non-target max ---------------------------------------------------
+    float mx = ztail;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) mx = fmaxf(mx, v[i].get(e));
+    mx = block_max<THREADS>(mx, red, 0);
+
+    // ---- non-target sum of exponentials ----------------------------------
+    double sd = 0.0;
+    if constexpr (LS) {
+        // With smoothing the gradient k (p_j - eps/V) cancels where p_j is
+        // close to eps/V and magnifies any error of lse there, so the sum is
+        // taken with fp64 exponentials and fp64 accumulation.
+        if (mx != ninf()) {
+            const double md = (double)mx;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) sd += exp((double)v[i].get(e) - md);
+            sd += exp((double)ztail - md);
+        }
+        sd = block_sum_d<THREADS>(sd, red, 0);
+        sz = block_sum_d<THREADS>(sz, red, 1);
+    } else {
+        float s = 0.0f;
+        if (mx != ninf()) {
+            const float K = mx * kL2E;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                float p[EPV];
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) p[e] = fast_exp2(fmaf(v[i].get(e), kL2E, -K));
+#pragma unroll
+                for (int h = EPV / 2; h > 0; h >>= 1)
+#pragma unroll
+                    for (int e = 0; e < h; ++e) p[e] += p[e + h];
+                s += p[0];
+            }
+            s += fast_exp2(fmaf(ztail, kL2E, -K));
+        }
+        s = block_sum<THREADS>(s, red, 1);
+        sd = (double)s;
+        if (mx != ninf()) {
+            // the terms were 2^(z kL2E - K) with K = fl(mx kL2E): undo the
+            // rounding of K (the residual r is exact)
+            const float K = mx * kL2E;
+            const float r = fmaf(mx, kL2E, -K);
+            sd *= exp2(-(double)r);
+        }
+    }
+
+    // ---- finalize (one thread, fp64) ---------------------------------------
+    if (tid == 0) {
+        const double zt = (double)In::load1(zrow + t * In::kSize);
+        const RowFinal f =
+            finalize_row((double)mx, sd, zt, sz, (double)V, (double)a.eps);
+        a.loss_rows[row] = (float)f.loss;
+        const double k = row_scale(a.reduction, a.grad_output, a.n_valid, row);
+        gc_sh = grad_constants(f.lse, f.gt, k, (double)a.eps, (double)V);
+    }
+    __syncthreads();
+    const GradConst c = gc_sh;
+
+    // ---- gradient sweep from registers ------------------------------------
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int64_t vi = (int64_t)i * THREADS + tid;
+        float g[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const float z = v[i].get(e);
+            g[e] = grad_elem<OUT, LS>(z, c);
+        }
+        if (t_in_vec && i == t_slot && wave == (t_owner >> 6)) {
+            if (lane == (t_owner & 63)) {
+#pragma unroll
+                for (int e = 0; e < EPV; ++e)
+                    if (e == te) g[e] = c.gk;
+            }
+        }
+        if (vi < nvec) St::put(grow + vi * EPV * kOutSize, g);
+    }
+    if (tid < ntail) {
+        float g;
+        if (!t_in_vec && tid == (int)(t - tail0))
+            g = c.gk;
+        else
+            g = grad_elem<OUT, LS>(ztail, c);
+        Store<OUT, 1>::put(grow + (tail0 + tid) * kOutSize, &g);
+    }
+}
+
+// ===========================================================================
+// streaming stats: one workgroup per (row, column chunk)
+// ===========================================================================
+
+// Per-thread online (max, sum of exponentials).  The fast form keeps the sum
+// in fp32 relative to K = fl(m kL2E); the precise form (label smoothing,
+// where the gradient needs lse to ~1e-12) uses fp64 exponentials and sums.
+template <bool PRECISE>
+struct Online;
+
+template <>
+struct Online<false> {
+    float m = -__builtin_inff(), K = -__builtin_inff(), s = 0.0f;
+    __device__ __forceinline__ void rescale(float vm) {
+        if (vm > m) {
+            const float K2 = vm * kL2E;
+            s = (m == ninf()) ? 0.0f : s * fast_exp2(K - K2);
+            m = vm;
+            K = K2;
+        }
+    }
+    __device__ __forceinline__ float term(float z) const { return fast_exp2(fmaf(z, kL2E, -K)); }
+    __device__ __forceinline__ void add(float t) { s += t; }
+    __device__ __forceinline__ MaxSum result() const {
+        if (m == ninf()) return {m, 0.0};
+        // undo the rounding of K (the residual is exact)
+        return {m, (double)s * exp2(-(double)fmaf(m, kL2E, -K))};
+    }
+};
+
+template <>
+struct Online<true> {
+    float m = -__builtin_inff();
+    double s = 0.0;
+    __device__ __forceinline__ void rescale(float vm) {
+        if (vm > m) {
+            s = (m == ninf()) ? 0.0 : s * exp((double)m - (double)vm);
+            m = vm;
+        }
+    }
+    __device__ __forceinline__ double term(float z) const { return exp((double)z - (double)m); }
+    __device__ __forceinline__ void add(double t) { s += t; }
+    __device__ __forceinline__ MaxSum result() const { return {m, s}; }
+};
+
+template <int IN, int EPV, int THREADS, int UNROLL, bool LS>
+__global__ __launch_bounds__(THREADS) void k_stats(StatsArgs a) {
+    using In = Elem<IN>;
+    using Ch = Chunk<IN, EPV>;
+    __shared__ BlockRed<THREADS> red;
+
+    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x / a.nchunks;
+    const int ch = (int)(blockIdx.x % a.nchunks);
+    const int64_t c0 = (int64_t)ch * a.chunk_cols;
+    const int64_t c1 = std::min(a.V_local, c0 + a.chunk_cols);
+    const int64_t t = a.target[row];
+    ce_row_stats *o = a.out + (int64_t)ch * a.T + row;
+
+    if (t == a.ignore_index || t < 0 || t >= a.V_total) {
+        // no row statistics are needed: the row is ignored or an error
+        if (tid == 0) {
+            ce_row_stats z;
+            z.m = ninf();
+            z.zt = 0.0f;
+            z.own = 0;
+            z.reserved = 0;
+            z.s = 0.0;
+            z.sz = 0.0;
+            *o = z;
+        }
+        return;
+    }
+    const int64_t tl = t - a.vocab_start; // target column in this call
+    const int64_t tc = (tl >= c0 && tl < c1) ? tl : -1;
+
+    const char *zrow = static_cast<const char *>(a.logits) + row * a.ld * In::kSize;
+    const int64_t nv = (c1 - c0) / EPV; // full vectors of this chunk
+    const int64_t tail0 = c0 + nv * EPV;
+
+    Online<LS> acc;
+    double sz = 0.0;
+    for (int64_t base = 0; base < nv; base += (int64_t)UNROLL * THREADS) {
+        Ch v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t vi = base + (int64_t)u * THREADS + tid;
+            if (vi < nv)
+                v[u].load(zrow + (c0 + vi * EPV) * In::kSize);
+            else
+                v[u].fill_ninf();
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t vi = base + (int64_t)u * THREADS + tid;
+            const int64_t col = c0 + vi * EPV;
+            if (LS && vi < nv) {
+                float p[EPV];
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) p[e] = v[u].get(e);
+#pragma unroll
+                for (int h = EPV / 2; h > 0; h >>= 1)
+#pragma unroll
+                    for (int e = 0; e < h; ++e) p[e] += p[e + h];
+                sz += (double)p[0];
+            }
+            if (tc >= col && tc < col + EPV) v[u].kill((int)(tc - col));
+            float vm = v[u].get(0);
+#pragma unroll
+            for (int e = 1; e < EPV; ++e) vm = fmaxf(vm, v[u].get(e));
+            acc.rescale(vm);
+            if (acc.m != ninf()) {
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) acc.add(acc.term(v[u].get(e)));
+            }
+        }
+    }
+    // scalar tail of the chunk
+    for (int64_t col = tail0 + tid; col < c1; col += THREADS) {
+        float z = In::load1(zrow + col * In::kSize);
+        if (LS) sz += (double)z;
+        if (col == tc) z = ninf();
+        acc.rescale(z);
+        if (acc.m != ninf()) acc.add(acc.term(z));
+    }
+    const MaxSum ms = block_combine<THREADS>(acc.result(), red);
+    if (LS) sz = block_sum_d<THREADS>(sz, red, 1);
+    if (tid == 0) {
+        ce_row_stats r;
+        r.m = ms.m;
+        r.zt = (tc >= 0) ? In::load1(zrow + tc * In::kSize) : 0.0f;
+        r.own = (tc >= 0) ? 1 : 0;
+        r.reserved = 0;
+        r.s = ms.s;
+        r.sz = sz;
+        *o = r;
+    }
+}
+
+// ===========================================================================
+// merge of partial statistics ([S][T], in order) + optional finalize
+// ===========================================================================
+
+constexpr int kMergeThreads = 256;
+
+__global__ __launch_bounds__(kMergeThreads) void k_merge(MergeArgs a) {
+    const int64_t r = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
+    if (r >= a.T) return;
+    double M = -__builtin_inf();
+    for (int k = 0; k < a.S; ++k) M = fmax(M, (double)a.in[(int64_t)k * a.T + r].m);
+    double s = 0.0, zt = 0.0, sz = 0.0;
+    int own = 0;
+    for (int k = 0; k < a.S; ++k) {
+        const ce_row_stats p = a.in[(int64_t)k * a.T + r];
+        if (p.m != ninf()) s += p.s * exp((double)p.m - M);
+        zt += (double)p.zt;
+        own += p.own;
+        sz += p.sz;
+    }
+    if (a.stats_out) {
+        ce_row_stats o;
+        o.m = (float)M;
+        o.zt = (float)zt;
+        o.own = own;
+        o.reserved = 0;
+        o.s = s;
+        o.sz = sz;
+        a.stats_out[r] = o;
+    }
+    if (a.fin || a.loss_rows) {
+        const int64_t t = a.target[r];
+        ce_row_final fo;
+        fo.lse = 0.0;
+        fo.gt = 0.0;
+        fo.m = 0.0f;
+        float loss;
+        if (t == a.ignore_index) {
+            fo.status = 0;
+            loss = 0.0f;
+        } else if (t < 0 || t >= a.V_total || own != 1) {
+            fo.status = -1;
+            loss = __builtin_nanf("");
+        } else {
+            const RowFinal f = finalize_row(M, s, zt, sz, (double)a.V_total, (double)a.eps);
+            fo.lse = f.lse;
+            fo.gt = f.gt;
+            fo.m = (float)M;
+            fo.status = 1;
+            loss = (float)f.loss;
+        }
+        if (a.fin) a.fin[r] = fo;
+        if (a.loss_rows) a.loss_rows[r] = loss;
+    }
+}
+
+// ===========================================================================
+// streaming gradient: one workgroup per (row, column chunk)
+// ===========================================================================
+
+template <int IN, int OUT, int EPV, int THREADS, int UNROLL, bool LS>
+__global__ __launch_bounds__(THREADS) void k_grad(GradArgs a) {
+    using In = Elem<IN>;
+    using Ch = Chunk<IN, EPV>;
+    using St = Store<OUT, EPV>;
+    constexpr int kOutSize = (OUT == CE_BF16) ? 2 : 4;
+    __shared__ GradConst gc_sh;
+
+    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x / a.nchunks;
+    const int ch = (int)(blockIdx.x % a.nchunks);
+    const int64_t c0 = (int64_t)ch * a.chunk_cols;
+    const int64_t c1 = std::min(a.V_local, c0 + a.chunk_cols);
+    const int64_t nv = (c1 - c0) / EPV;
+    const int64_t tail0 = c0 + nv * EPV;
+    const char *zrow = static_cast<const char *>(a.logits) + row * a.ld * In::kSize;
+    char *grow = static_cast<char *>(a.grad) + row * a.ldg * kOutSize;
+
+    const ce_row_final f = a.fin[row];
+    if (f.status != 1) {
+        float zero[EPV];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) zero[e] = 0.0f;
+        for (int64_t vi = tid; vi < nv; vi += THREADS) St::put(grow + (c0 + vi * EPV) * kOutSize, zero);
+        for (int64_t col = tail0 + tid; col < c1; col += THREADS)
+            Store<OUT, 1>::put(grow + col * kOutSize, zero);
+        return;
+    }
+    if (tid == 0) {
+        const double k = row_scale(a.reduction, a.grad_output, a.n_valid, row);
+        gc_sh = grad_constants(f.lse, f.gt, k, (double)a.eps, (double)a.V_total);
+    }
+    __syncthreads();
+    const GradConst c = gc_sh;
+    const int64_t tl = a.target[row] - a.vocab_start;
+    const int64_t tc = (tl >= c0 && tl < c1) ? tl : -1;
+
+    for (int64_t base = 0; base < nv; base += (int64_t)UNROLL * THREADS) {
+        Ch v[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t vi = base + (int64_t)u * THREADS + tid;
+            if (vi < nv) v[u].load(zrow + (c0 + vi * EPV) * In::kSize);
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const int64_t vi = base + (int64_t)u * THREADS + tid;
+            if (vi >= nv) continue;
+            const int64_t col = c0 + vi * EPV;
+            float g[EPV];
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) g[e] = grad_elem<OUT, LS>(v[u].get(e), c);
+            if (tc >= col && tc < col + EPV) {
+#pragma unroll
+                for (int e = 0; e < EPV; ++e)
+                    if (col + e == tc) g[e] = c.gk;
+            }
+            St::put(grow + col * kOutSize, g);
+        }
+    }
+    for (int64_t col = tail0 + tid; col < c1; col += THREADS) {
+        const float z = In::load1(zrow + col * In::kSize);
+        float g;
+        g = (col == tc) ? c.gk : grad_elem<OUT, LS>(z, c);
+        Store<OUT, 1>::put(grow + col * kOutSize, &g);
+    }
+}
+
+} // namespace vce
+
+// ===========================================================================
+// launchers
+// ===========================================================================
+namespace vce {
+
+hipError_t launch_count(const int64_t *target, int64_t T, int64_t ignore_index, int64_t V_total,
+                        int32_t *n_valid, int32_t *err_count, hipStream_t stream) {
+    hipLaunchKernelGGL(k_count, dim3(1), dim3(kCountThreads), 0, stream, target, T, ignore_index,
+                       V_total, n_valid, err_count);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce(const float *loss_rows, int64_t T, int reduction, const int32_t *n_valid,
+                         float *loss, hipStream_t stream) {
+    hipLaunchKernelGGL(k_reduce, dim3(1), dim3(kReduceThreads), 0, stream, loss_rows, T,
+                       reduction, n_valid, loss);
+    return hipGetLastError();
+}
+
+// (threads, vectors per thread) of the row-resident kernel, smallest first
+struct ResidentShape {
+    int threads, nv;
+};
+constexpr ResidentShape kResident[] = {{256, 1}, {256, 2},  {256, 4},  {256, 8},
+                                       {256, 16}, {512, 16}, {1024, 16}};
+
+static int resident_index(int in_dt, int64_t V) {
+    const int64_t epv = (in_dt == CE_BF16) ? 8 : 4;
+    const int64_t nvec = V / epv;
+    for (int i = 0; i < (int)(sizeof(kResident) / sizeof(kResident[0])); ++i)
+        if ((int64_t)kResident[i].threads * kResident[i].nv >= nvec &&
+            kResident[i].threads >= V - nvec * epv)
+            return i;
+    return -1;
+}
+
+int resident_threads(int in_dt, int64_t V) {
+    const int i = resident_index(in_dt, V);
+    return i < 0 ? 0 : kResident[i].threads;
+}
+
+template <int IN, int OUT, bool LS>
+static hipError_t fused_dispatch(const FusedArgs &a, int64_t T, hipStream_t stream) {
+    const int i = resident_index(IN, a.V);
+    const dim3 grid((unsigned)T);
+#define VCE_RES(TH, NV)                                                                         \
+    hipLaunchKernelGGL((k_fused_resident<IN, OUT, TH, NV, LS>), grid, dim3(TH), 0, stream, a); \
+    break;
+    switch (i) {
+    case 0: VCE_RES(256, 1)
+    case 1: VCE_RES(256, 2)
+    case 2: VCE_RES(256, 4)
+    case 3: VCE_RES(256, 8)
+    case 4: VCE_RES(256, 16)
+    case 5: VCE_RES(512, 16)
+    case 6: VCE_RES(1024, 16)
+    default: return hipErrorInvalidValue;
+    }
+#undef VCE_RES
+    return hipGetLastError();
+}
+
+hipError_t launch_fused_resident(const FusedArgs &a, int in_dt, int out_dt, int64_t T,
+                                 hipStream_t stream) {
+    const bool ls = a.eps > 0.0f;
+    if (in_dt == CE_BF16) {
+        if (out_dt == CE_BF16)
+            return ls ? fused_dispatch<CE_BF16, CE_BF16, true>(a, T, stream)
+                      : fused_dispatch<CE_BF16, CE_BF16, false>(a, T, stream);
+        return ls ? fused_dispatch<CE_BF16, CE_F32, true>(a, T, stream)
+                  : fused_dispatch<CE_BF16, CE_F32, false>(a, T, stream);
+    }
+    if (out_dt == CE_BF16)
+        return ls ? fused_dispatch<CE_F32, CE_BF16, true>(a, T, stream)
+                  : fused_dispatch<CE_F32, CE_BF16, false>(a, T, stream);
+    return ls ? fused_dispatch<CE_F32, CE_F32, true>(a, T, stream)
+              : fused_dispatch<CE_F32, CE_F32, false>(a, T, stream);
+}
+
+constexpr int kStreamThreads = 256;
+constexpr int kStreamUnroll = 4;
+
+template <int IN, bool LS>
+static void stats_dispatch(const StatsArgs &a, bool vec, dim3 grid, hipStream_t stream) {
+    constexpr int EPV = Elem<IN>::kVec;
+    if (vec)
+        hipLaunchKernelGGL((k_stats<IN, EPV, kStreamThreads, kStreamUnroll, LS>), grid,
+                           dim3(kStreamThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_stats<IN, 1, kStreamThreads, 16, LS>), grid, dim3(kStreamThreads),
+                           0, stream, a);
+}
+
+hipError_t launch_stats(const StatsArgs &a, int in_dt, bool vec, hipStream_t stream) {
+    const dim3 grid((unsigned)(a.T * a.nchunks));
+    const bool ls = a.smoothing != 0;
+    if (in_dt == CE_BF16)
+        ls ? stats_dispatch<CE_BF16, true>(a, vec, grid, stream)
+           : stats_dispatch<CE_BF16, false>(a, vec, grid, stream);
+    else
+        ls ? stats_dispatch<CE_F32, true>(a, vec, grid, stream)
+           : stats_dispatch<CE_F32, false>(a, vec, grid, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs &a, hipStream_t stream) {
+    const dim3 grid((unsigned)((a.T + kMergeThreads - 1) / kMergeThreads));
+    hipLaunchKernelGGL(k_merge, grid, dim3(kMergeThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int IN, int OUT, bool LS>
+static void grad_dispatch(const GradArgs &a, bool vec, dim3 grid, hipStream_t stream) {
+    constexpr int EPV = Elem<IN>::kVec;
+    if (vec)
+        hipLaunchKernelGGL((k_grad<IN, OUT, EPV, kStreamThreads, kStreamUnroll, LS>), grid,
+                           dim3(kStreamThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((k_grad<IN, OUT, 1, kStreamThreads, 16, LS>), grid,
+                           dim3(kStreamThreads), 0, stream, a);
+}
+
+hipError_t launch_grad(const GradArgs &a, int in_dt, int out_dt, bool vec, int64_t T,
+                       hipStream_t stream) {
+    const dim3 grid((unsigned)(T * a.nchunks));
+    const bool ls = a.eps > 0.0f;
+    if (in_dt == CE_BF16) {
+        if (out_dt == CE_BF16)
+            ls ? grad_dispatch<CE_BF16, CE_BF16, true>(a, vec, grid, stream)
+               : grad_dispatch<CE_BF16, CE_BF16, false>(a, vec, grid, stream);
+        else
+            ls ? grad_dispatch<CE_BF16, CE_F32, true>(a, vec, grid, stream)
+               : grad_dispatch<CE_BF16, CE_F32, false>(a, vec, grid, stream);
+    } else {
+        if (out_dt == CE_BF16)
+            ls ? grad_dispatch<CE_F32, CE_BF16, true>(a, vec, grid, stream)
+               : grad_dispatch<CE_F32, CE_BF16, false>(a, vec, grid, stream);
+        else
+            ls ? grad_dispatch<CE_F32, CE_F32, true>(a, vec, grid, stream)
+               : grad_dispatch<CE_F32, CE_F32, false>(a, vec, grid, stream);
+    }
+    return hipGetLastError();
+}
+
+} // namespace vce
