@@ -28,9 +28,25 @@ __device__ __forceinline__ float ninf() { return -__builtin_inff(); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-struct alignas(16) U4 {
-    uint32_t w[4];
-};
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 16-byte loads and stores; NT = non-temporal (streamed once, kept out of
+// the caches as far as the hardware allows)
+template <bool NT>
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(static_cast<const u32x4 *>(p));
+    else
+        return *static_cast<const u32x4 *>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st16(void *p, u32x4 v) {
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, static_cast<u32x4 *>(p));
+    else
+        *static_cast<u32x4 *>(p) = v;
+}
 
 // ---------------------------------------------------------------------------
 // A group of EPV consecutive logits of one row, kept in their storage format.
@@ -41,11 +57,16 @@ struct Chunk;
 template <>
 struct Chunk<CE_BF16, 8> {
     static constexpr int kBytes = 16;
-    U4 v;
-    __device__ __forceinline__ void load(const void *p) { v = *static_cast<const U4 *>(p); }
-    __device__ __forceinline__ void fill_ninf() { v.w[0] = v.w[1] = v.w[2] = v.w[3] = 0xff80ff80u; }
+    u32x4 v;
+    // Makes the packed words opaque to the compiler, so values unpacked in
+    // one sweep are not kept alive for the next (that would double the
+    // registers a resident row needs).
+    __device__ __forceinline__ void fence() { asm volatile("" : "+v"(v)); }
+    template <bool NT = false>
+    __device__ __forceinline__ void load(const void *p) { v = ld16<NT>(p); }
+    __device__ __forceinline__ void fill_ninf() { v = u32x4{0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u}; }
     __device__ __forceinline__ float get(int e) const {
-        const uint32_t x = v.w[e >> 1];
+        const uint32_t x = v[e >> 1];
         return __uint_as_float((e & 1) ? (x & 0xffff0000u) : (x << 16));
     }
     // e may be a run-time value: every word is visited with a select, so the
@@ -54,20 +75,22 @@ struct Chunk<CE_BF16, 8> {
         const uint32_t keep = (e & 1) ? 0x0000ffffu : 0xffff0000u;
         const uint32_t put = (e & 1) ? 0xff800000u : 0x0000ff80u;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v.w[k] = (k == (e >> 1)) ? ((v.w[k] & keep) | put) : v.w[k];
+        for (int k = 0; k < 4; ++k) v[k] = (k == (e >> 1)) ? ((v[k] & keep) | put) : v[k];
     }
 };
 
 template <>
 struct Chunk<CE_F32, 4> {
     static constexpr int kBytes = 16;
-    U4 v;
-    __device__ __forceinline__ void load(const void *p) { v = *static_cast<const U4 *>(p); }
-    __device__ __forceinline__ void fill_ninf() { v.w[0] = v.w[1] = v.w[2] = v.w[3] = 0xff800000u; }
-    __device__ __forceinline__ float get(int e) const { return __uint_as_float(v.w[e]); }
+    u32x4 v;
+    __device__ __forceinline__ void fence() { asm volatile("" : "+v"(v)); }
+    template <bool NT = false>
+    __device__ __forceinline__ void load(const void *p) { v = ld16<NT>(p); }
+    __device__ __forceinline__ void fill_ninf() { v = u32x4{0xff800000u, 0xff800000u, 0xff800000u, 0xff800000u}; }
+    __device__ __forceinline__ float get(int e) const { return __uint_as_float(v[e]); }
     __device__ __forceinline__ void kill(int e) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) v.w[k] = (k == e) ? 0xff800000u : v.w[k];
+        for (int k = 0; k < 4; ++k) v[k] = (k == e) ? 0xff800000u : v[k];
     }
 };
 
@@ -75,6 +98,7 @@ template <>
 struct Chunk<CE_BF16, 1> {
     static constexpr int kBytes = 2;
     uint32_t v;
+    template <bool NT = false>
     __device__ __forceinline__ void load(const void *p) {
         v = (uint32_t)(*static_cast<const uint16_t *>(p)) << 16;
     }
@@ -87,6 +111,7 @@ template <>
 struct Chunk<CE_F32, 1> {
     static constexpr int kBytes = 4;
     uint32_t v;
+    template <bool NT = false>
     __device__ __forceinline__ void load(const void *p) { v = *static_cast<const uint32_t *>(p); }
     __device__ __forceinline__ void fill_ninf() { v = 0xff800000u; }
     __device__ __forceinline__ float get(int) const { return __uint_as_float(v); }
@@ -125,22 +150,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, b);
 }
 
-template <int DT, int N>
+template <int DT, int N, bool NT = false>
 struct Store;
 
-template <int N>
-struct Store<CE_BF16, N> {
+template <int N, bool NT>
+struct Store<CE_BF16, N, NT> {
     __device__ __forceinline__ static void put(void *p, const float *g) {
         if constexpr (N == 8) {
-            U4 o;
+            u32x4 o;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) o.w[i] = pack_bf16x2(g[2 * i], g[2 * i + 1]);
-            *static_cast<U4 *>(p) = o;
+            for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(g[2 * i], g[2 * i + 1]);
+            st16<NT>(p, o);
         } else if constexpr (N == 4) {
-            uint2 o;
-            o.x = pack_bf16x2(g[0], g[1]);
-            o.y = pack_bf16x2(g[2], g[3]);
-            *static_cast<uint2 *>(p) = o;
+            u32x2 o;
+            o[0] = pack_bf16x2(g[0], g[1]);
+            o[1] = pack_bf16x2(g[2], g[3]);
+            *static_cast<u32x2 *>(p) = o;
         } else {
             static_assert(N == 1, "unsupported width");
             *static_cast<uint16_t *>(p) = (uint16_t)(pack_bf16x2(g[0], 0.0f) & 0xffffu);
@@ -148,23 +173,23 @@ struct Store<CE_BF16, N> {
     }
 };
 
-template <int N>
-struct Store<CE_F32, N> {
+template <int N, bool NT>
+struct Store<CE_F32, N, NT> {
     __device__ __forceinline__ static void put(void *p, const float *g) {
         if constexpr (N == 8) {
-            U4 a, b;
+            u32x4 a, b;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                a.w[i] = __float_as_uint(g[i]);
-                b.w[i] = __float_as_uint(g[4 + i]);
+                a[i] = __float_as_uint(g[i]);
+                b[i] = __float_as_uint(g[4 + i]);
             }
-            static_cast<U4 *>(p)[0] = a;
-            static_cast<U4 *>(p)[1] = b;
+            st16<NT>(p, a);
+            st16<NT>(static_cast<char *>(p) + 16, b);
         } else if constexpr (N == 4) {
-            U4 a;
+            u32x4 a;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a.w[i] = __float_as_uint(g[i]);
-            *static_cast<U4 *>(p) = a;
+            for (int i = 0; i < 4; ++i) a[i] = __float_as_uint(g[i]);
+            st16<NT>(p, a);
         } else {
             static_assert(N == 1, "unsupported width");
             *static_cast<float *>(p) = g[0];
@@ -318,6 +343,54 @@ __device__ inline RowFinal finalize_row(double m, double s, double zt, double sz
     const double gt = (pt < 0.25) ? pt - 1.0 : -1.0 / (1.0 + exp(-f.x));
     f.gt = gt + eps * (V - 1.0) / V;
     f.loss = (eps == 0.0) ? f.nll : (1.0 - eps) * f.nll + eps * (f.lse - sz / V);
+    return f;
+}
+
+// Finalize in fp32 for the fast path (bf16 gradients, no smoothing): the
+// same steps as finalize_row with binary32 transcendentals, which keeps the
+// register footprint small while the whole row is held in registers.  The
+// loss gets about 1e-6 relative error (x carries the error of log s) and
+// the gradient exponent about 2e-6; both sit far inside the per-row loss
+// tolerance and a bf16 ulp.
+struct FastFinal {
+    float loss, cb, scale, gk;
+};
+
+__device__ inline FastFinal finalize_fast(float m, float s, float zt, double k) {
+    const float inf = __builtin_inff();
+    float x;
+    if (s == 0.0f)
+        x = (zt == -inf) ? __builtin_nanf("") : -inf;
+    else if (zt == -inf)
+        x = inf;
+    else
+        x = (m - zt) + logf(s);
+    float nll;
+    if (x == -inf)
+        nll = 0.0f;
+    else if (x == inf)
+        nll = inf;
+    else
+        nll = fmaxf(x, 0.0f) + log1pf(expf(-fabsf(x)));
+    const float lse = (zt == -inf) ? m + logf(s) : zt + nll;
+    const float pt = 1.0f / (1.0f + expf(x));
+    const float gt = (pt < 0.25f) ? pt - 1.0f : -1.0f / (1.0f + expf(-x));
+    FastFinal f;
+    f.loss = nll;
+    f.gk = (float)(k * (double)gt);
+    // 2^(z kL2E - cb) * scale = k exp(z - lse): cb = lse kL2E - B and
+    // scale = k 2^-B times the rounding residual of cb (a few fp64 ops)
+    int B = 64;
+    const double ka = fabs(k);
+    if (ka > 0.0 && ka < __builtin_inf()) {
+        const int ek = ilogb(ka);
+        B = ek + 120;
+        B = B > 100 ? 100 : (B < 0 ? 0 : B);
+    }
+    const double C = (double)lse * kL2E_d;
+    f.cb = (float)(C - (double)B);
+    const double d = ((double)f.cb - (C - (double)B)) * 0.6931471805599453; // |d| < 1e-5
+    f.scale = (float)(ldexp(k, -B) * (1.0 + d * (1.0 + 0.5 * d)));
     return f;
 }
 

@@ -93,71 +93,75 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const float *__restri
 // fused, row resident
 // ===========================================================================
 
+// One workgroup per row; the row lives in registers from its load to its
+// gradient store.  FAST = bf16 gradient without smoothing: fp32 finalize
+// and the biased exponent form (see GradConst); otherwise fp64 finalize.
 template <int IN, int OUT, int THREADS, int NV, bool LS>
 __global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
     using In = Elem<IN>;
     constexpr int EPV = In::kVec;
     using Ch = Chunk<IN, EPV>;
-    using St = Store<OUT, EPV>;
+    using St = Store<OUT, EPV, true>;
     constexpr int kOutSize = (OUT == CE_BF16) ? 2 : 4;
+    constexpr bool FAST = (OUT == CE_BF16) && !LS;
 
     __shared__ BlockRed<THREADS> red;
     __shared__ GradConst gc_sh;
 
     const int tid = threadIdx.x;
-    const int wave = tid / kWave;
-    const int lane = tid & (kWave - 1);
     const int64_t row = blockIdx.x;
-    const int64_t V = a.V;
-    const int64_t nvec = V / EPV;
-    const int64_t tail0 = nvec * EPV;
-    const int ntail = (int)(V - tail0);
+    const int V = (int)a.V;
+    const int nvec = V / EPV;
+    const int tail0 = nvec * EPV;
+    const int ntail = V - tail0;
     const char *zrow = static_cast<const char *>(a.logits) + row * a.ld * In::kSize;
     char *grow = static_cast<char *>(a.grad) + row * a.ldg * kOutSize;
 
-    const int64_t t = a.target[row];
-    if (t == a.ignore_index || t < 0 || t >= V) {
+    const int64_t t64 = a.target[row];
+    if (t64 == a.ignore_index || t64 < 0 || t64 >= V) {
         // ignored row or bad target: zero gradient, no reads of the row
         float zero[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) zero[e] = 0.0f;
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int64_t vi = (int64_t)i * THREADS + tid;
+            const int vi = i * THREADS + tid;
             if (vi < nvec) St::put(grow + vi * EPV * kOutSize, zero);
         }
         if (tid < ntail) Store<OUT, 1>::put(grow + (tail0 + tid) * kOutSize, zero);
-        if (tid == 0) a.loss_rows[row] = (t == a.ignore_index) ? 0.0f : __builtin_nanf("");
+        if (tid == 0) a.loss_rows[row] = (t64 == a.ignore_index) ? 0.0f : __builtin_nanf("");
         return;
     }
+    const int t = (int)t64;
 
-    // ---- load the row into registers -------------------------------------
+    // ---- load the row into registers (streamed: read once) ----------------
     Ch v[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int64_t vi = (int64_t)i * THREADS + tid;
+        const int vi = i * THREADS + tid;
         if (vi < nvec)
-            v[i].load(zrow + vi * EPV * In::kSize);
+            v[i].template load<true>(zrow + vi * EPV * In::kSize);
         else
             v[i].fill_ninf();
     }
     float ztail = ninf();
     if (tid < ntail) ztail = In::load1(zrow + (tail0 + tid) * In::kSize);
 
-    // where the target sits: vector tv (slot tv / THREADS of thread
-    // tv % THREADS) and element te, or in the scalar tail
-    const int64_t tv = t / EPV;
-    const int te = (int)(t % EPV);
+    // where the target sits: vector tv = slot t_slot of thread t_owner, or
+    // the scalar tail.  t is the same for the whole workgroup, so the slot
+    // tests below are scalar branches; only the owner lane does any work.
+    const int tv = t / EPV;
+    const int te = t - tv * EPV;
     const bool t_in_vec = t < tail0;
-    const int t_slot = (int)(tv / THREADS);
-    const int t_owner = (int)(tv % THREADS);
+    const int t_slot = tv / THREADS;
+    const bool t_owner = t_in_vec && (tid == tv - t_slot * THREADS);
 
     // ---- sum of the whole row (smoothing only), before the target is masked
     double sz = 0.0;
     if constexpr (LS) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
-            const int64_t vi = (int64_t)i * THREADS + tid;
+            const int vi = i * THREADS + tid;
             float p[EPV];
 #pragma unroll
             for (int e = 0; e < EPV; ++e) p[e] = v[i].get(e);
@@ -170,16 +174,16 @@ __global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
         if (tid < ntail) sz += (double)ztail;
     }
 
-    // ---- drop the target before any reduction (it sits in one lane) ------
-    if (t_in_vec) {
-        if (wave == (t_owner >> 6)) {
+    // ---- drop the target before any reduction ------------------------------
+    if (t_owner) {
 #pragma unroll
-            for (int i = 0; i < NV; ++i)
-                if (i == t_slot && lane == (t_owner & 63)) v[i].kill(te);
-        }
-    } else if (tid == (int)(t - tail0)) {
-        ztail = ninf();
+        for (int i = 0; i < NV; ++i)
+            if (i == t_slot) v[i].kill(te);
     }
+    if (!t_in_vec && tid == t - tail0) ztail = ninf();
+
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i].fence();
 
     // ---- non-target max ---------------------------------------------------
     float mx = ztail;
@@ -188,9 +192,12 @@ __global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
 #pragma unroll
         for (int e = 0; e < EPV; ++e) mx = fmaxf(mx, v[i].get(e));
     mx = block_max<THREADS>(mx, red, 0);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i].fence();
 
     // ---- non-target sum of exponentials ----------------------------------
     double sd = 0.0;
+    float s = 0.0f;
     if constexpr (LS) {
         // With smoothing the gradient k (p_j - eps/V) cancels where p_j is
         // close to eps/V and magnifies any error of lse there, so the sum is
@@ -206,7 +213,6 @@ __global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
         sd = block_sum_d<THREADS>(sd, red, 0);
         sz = block_sum_d<THREADS>(sz, red, 1);
     } else {
-        float s = 0.0f;
         if (mx != ninf()) {
             const float K = mx * kL2E;
 #pragma unroll
@@ -223,53 +229,56 @@ __global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
             s += fast_exp2(fmaf(ztail, kL2E, -K));
         }
         s = block_sum<THREADS>(s, red, 1);
-        sd = (double)s;
         if (mx != ninf()) {
             // the terms were 2^(z kL2E - K) with K = fl(mx kL2E): undo the
-            // rounding of K (the residual r is exact)
+            // rounding of K (the residual is exact)
             const float K = mx * kL2E;
-            const float r = fmaf(mx, kL2E, -K);
-            sd *= exp2(-(double)r);
+            s *= fast_exp2(-fmaf(mx, kL2E, -K));
         }
+        sd = (double)s;
     }
 
-    // ---- finalize (one thread, fp64) ---------------------------------------
+    // ---- finalize (one thread) -----------------------------------------------
     if (tid == 0) {
-        const double zt = (double)In::load1(zrow + t * In::kSize);
-        const RowFinal f =
-            finalize_row((double)mx, sd, zt, sz, (double)V, (double)a.eps);
-        a.loss_rows[row] = (float)f.loss;
+        const float zt = In::load1(zrow + (int64_t)t * In::kSize);
         const double k = row_scale(a.reduction, a.grad_output, a.n_valid, row);
-        gc_sh = grad_constants(f.lse, f.gt, k, (double)a.eps, (double)V);
+        if constexpr (FAST) {
+            const FastFinal f = finalize_fast(mx, s, zt, k);
+            a.loss_rows[row] = f.loss;
+            GradConst c;
+            c.cb = f.cb;
+            c.scale = f.scale;
+            c.gk = f.gk;
+            c.ch = c.cl = c.k = c.ku = c.lu = c.d2hi = c.d2lo = 0.0f;
+            gc_sh = c;
+        } else {
+            const RowFinal f =
+                finalize_row((double)mx, sd, (double)zt, sz, (double)V, (double)a.eps);
+            a.loss_rows[row] = (float)f.loss;
+            gc_sh = grad_constants(f.lse, f.gt, k, (double)a.eps, (double)V);
+        }
     }
     __syncthreads();
     const GradConst c = gc_sh;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i].fence();
 
     // ---- gradient sweep from registers ------------------------------------
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int64_t vi = (int64_t)i * THREADS + tid;
+        const int vi = i * THREADS + tid;
         float g[EPV];
 #pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-            const float z = v[i].get(e);
-            g[e] = grad_elem<OUT, LS>(z, c);
-        }
-        if (t_in_vec && i == t_slot && wave == (t_owner >> 6)) {
-            if (lane == (t_owner & 63)) {
+        for (int e = 0; e < EPV; ++e) g[e] = grad_elem<OUT, LS>(v[i].get(e), c);
+        if (i == t_slot && t_owner) {
 #pragma unroll
-                for (int e = 0; e < EPV; ++e)
-                    if (e == te) g[e] = c.gk;
-            }
+            for (int e = 0; e < EPV; ++e)
+                if (e == te) g[e] = c.gk;
         }
         if (vi < nvec) St::put(grow + vi * EPV * kOutSize, g);
     }
     if (tid < ntail) {
-        float g;
-        if (!t_in_vec && tid == (int)(t - tail0))
-            g = c.gk;
-        else
-            g = grad_elem<OUT, LS>(ztail, c);
+        const float g = (!t_in_vec && tid == t - tail0) ? c.gk : grad_elem<OUT, LS>(ztail, c);
         Store<OUT, 1>::put(grow + (tail0 + tid) * kOutSize, &g);
     }
 }
