@@ -37,6 +37,9 @@
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
@@ -394,4 +397,14 @@ void oracle_to_bf16(const double *v, int64_t n, uint16_t *out)
             w = 0x7fc00000u | (w & 0x80000000u);
         out[i] = (uint16_t)(w >> 16);
     }
+}
+
+/* Number of OpenMP threads the row loops above run on. */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

@@ -53,6 +53,8 @@ def _load():
         lib.oracle_reduce.restype = d
         lib.oracle_to_bf16.argtypes = [P, i64, P]
         lib.oracle_to_bf16.restype = None
+        lib.oracle_threads.argtypes = []
+        lib.oracle_threads.restype = i
         _lib = lib
     return _lib
 
@@ -193,3 +195,8 @@ def bf16_to_f64(bits):
     bits = np.asarray(bits, np.uint16)
     with np.errstate(invalid="ignore"):
         return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def threads():
+    """OpenMP threads the oracle's row loops use."""
+    return int(_load().oracle_threads())
