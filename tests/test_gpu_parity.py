@@ -360,3 +360,39 @@ def test_api_errors_raise():
         vce.fused_fwd_bwd(logits, target, label_smoothing=1.0)
     with pytest.raises(vce.CEError):
         vce.fused_fwd_bwd(logits, target, grad=logits)   # grad aliases logits
+
+
+# --------------------------------------------------------------------------
+# writes stay inside [T, V] of the gradient view
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,V,in_dt,out_dt", [
+    (520, 128256, torch.bfloat16, torch.bfloat16),   # register + LDS rows, 2 per CU
+    (520, 128257, torch.bfloat16, torch.bfloat16),   # ... with a scalar tail
+    (520, 100003, torch.bfloat16, torch.float32),
+    (520, 40001, torch.float32, torch.bfloat16),
+    (520, 3000, torch.bfloat16, torch.bfloat16),     # register-resident rows
+    (520, 64128, torch.bfloat16, torch.bfloat16),
+    (24, 128256, torch.bfloat16, torch.bfloat16),    # split-V grid
+])
+def test_writes_stay_inside_the_gradient_rows(T, V, in_dt, out_dt):
+    """The gradient rows sit in a larger buffer (row stride V + 64, one
+    extra row) filled with a NaN-payload canary; after the call every
+    element outside the [T, V] view still holds it, and the view matches
+    the oracle."""
+    base = S.PAGE if in_dt == torch.bfloat16 else S.TINY
+    c, logits, target = _case(base, T, V, 500 + V % 97)
+    pad = 64
+    canary = 0x7FC5 if out_dt == torch.bfloat16 else 0x7FC00005
+    ity = torch.int16 if out_dt == torch.bfloat16 else torch.int32
+    buf = torch.full((T + 1, V + pad), canary, dtype=ity, device=DEV).view(out_dt)
+    g = buf[:T, :V]
+    _say(f"[canary] T={T} V={V} {in_dt}->{out_dt}")
+    out = vce.fused_fwd_bwd(logits, target, grad=g)
+    torch.cuda.synchronize()
+    raw = buf.view(ity)
+    assert torch.all(raw[:T, V:] == canary), "write past the end of a row"
+    assert torch.all(raw[T] == canary), "write past the last row"
+    ref = P.oracle_for(logits, target)
+    P.assert_grad_close(out["grad"], ref["grad"], f"canary view T={T} V={V}")
+    P.assert_loss_rows(out["loss_rows"], ref, "canary")

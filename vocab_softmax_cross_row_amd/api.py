@@ -39,6 +39,18 @@ def _grad_output(grad_output, reduction, T, device):
     return go
 
 
+def _grad_dtype(grad, grad_dtype, logits):
+    """The gradient dtype: that of a given buffer (which must agree with
+    grad_dtype if both are given), else grad_dtype, else the logits'."""
+    if grad is not None:
+        if grad_dtype is not None and grad_dtype != grad.dtype:
+            raise ValueError(f"grad is {grad.dtype} but grad_dtype={grad_dtype}")
+        if grad.dim() != 2 or grad.stride(1) != 1 or tuple(grad.shape) != tuple(logits.shape):
+            raise ValueError("grad must be a [T, V] view with contiguous rows")
+        return grad.dtype
+    return grad_dtype or logits.dtype
+
+
 def _workspace(prob, op, device):
     n = B.ce_workspace_bytes(prob, op)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device), n
@@ -50,7 +62,7 @@ def fused_fwd_bwd(logits, target, *, ignore_index=-100, label_smoothing=0.0, red
     T, V, ld = _logits2d(logits)
     target = _target(target, T)
     dev = logits.device
-    gdt = grad_dtype or logits.dtype
+    gdt = _grad_dtype(grad, grad_dtype, logits)
     if grad is None:
         grad = torch.empty((T, V), dtype=gdt, device=dev)
     ldg = grad.stride(0) if T > 1 else V
@@ -98,8 +110,8 @@ def forward(logits, target, *, vocab_start=0, V_total=None, ignore_index=-100,
 
 def merge_shard_stats(shard_stats, target, V_total, *, ignore_index=-100, label_smoothing=0.0,
                       reduction="mean", stream=None):
-    """Merge per-shard statistics (a list of [T, 24] buffers in shard order,
-    or one [S, T, 24] buffer) and finalize."""
+    """Merge per-shard statistics (a list of [T, 32] byte buffers in shard
+    order, or one [S, T, 32] buffer) and finalize."""
     if isinstance(shard_stats, (list, tuple)):
         shard_stats = torch.stack(list(shard_stats))
     S, T = shard_stats.shape[0], shard_stats.shape[1]
@@ -127,7 +139,7 @@ def backward(logits, target, fin, n_valid, *, grad_output=None, vocab_start=0, V
     target = _target(target, T)
     dev = logits.device
     V_total = V if V_total is None else V_total
-    gdt = grad_dtype or logits.dtype
+    gdt = _grad_dtype(grad, grad_dtype, logits)
     if grad is None:
         grad = torch.empty((T, V), dtype=gdt, device=dev)
     ldg = grad.stride(0) if T > 1 else V
