@@ -24,6 +24,19 @@ constexpr float kL2E_lo = (float)(kLog2e - kL2E_d);
 
 constexpr int kWave = 64;
 
+// Workgroups are dispatched round-robin over the 8 XCDs of an MI355X
+// (workgroup b runs on XCD b % 8), each with its own L2.  xcd_major maps
+// workgroup b of n to the unit that puts consecutive units on one XCD:
+// XCD x takes units [x q + min(x, r), ...) in order (q = n / 8, r = n % 8),
+// so each XCD streams one contiguous range of rows instead of all eight
+// interleaving at row granularity.  A bijection on [0, n) for any n.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int64_t xcd_major(int64_t b, int64_t n) {
+    const int64_t x = b % kXcds, j = b / kXcds;
+    const int64_t q = n / kXcds, r = n % kXcds;
+    return x * q + (x < r ? x : r) + j;
+}
+
 __device__ __forceinline__ float ninf() { return -__builtin_inff(); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

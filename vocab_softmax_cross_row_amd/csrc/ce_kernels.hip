@@ -33,23 +33,32 @@ namespace vce {
 // ===========================================================================
 // count: N_valid and bad targets (one workgroup, any T)
 // ===========================================================================
+// Each thread issues kPerThread independent target loads per round, so the
+// whole batch is in flight at once instead of one round trip per target.
 constexpr int kCountThreads = 1024;
+constexpr int kPerThread = 16;
 
 __global__ __launch_bounds__(kCountThreads) void k_count(const int64_t *__restrict__ target,
                                                          int64_t T, int64_t ignore_index,
                                                          int64_t V_total, int32_t *n_valid,
                                                          int32_t *err_count) {
-    __shared__ BlockRed<kCountThreads> red;
     int nv = 0, nb = 0;
-    for (int64_t r = threadIdx.x; r < T; r += kCountThreads) {
-        const int64_t t = target[r];
-        if (t == ignore_index) continue;
-        if (t >= 0 && t < V_total)
-            ++nv;
-        else
-            ++nb;
+    for (int64_t base = 0; base < T; base += (int64_t)kCountThreads * kPerThread) {
+        int64_t t[kPerThread];
+#pragma unroll
+        for (int u = 0; u < kPerThread; ++u) {
+            const int64_t r = base + (int64_t)u * kCountThreads + threadIdx.x;
+            t[u] = (r < T) ? target[r] : ignore_index;
+        }
+#pragma unroll
+        for (int u = 0; u < kPerThread; ++u) {
+            if (t[u] == ignore_index) continue;
+            if (t[u] >= 0 && t[u] < V_total)
+                ++nv;
+            else
+                ++nb;
+        }
     }
-    // two integer sums through the float slots would lose bits: use waves
     nv = wave_sum(nv);
     nb = wave_sum(nb);
     __shared__ int part[2][kCountThreads / kWave];
@@ -60,15 +69,14 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const int64_t *__restri
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        int a = 0, b = 0;
+        int x = 0, y = 0;
         for (int i = 0; i < kCountThreads / kWave; ++i) {
-            a += part[0][i];
-            b += part[1][i];
+            x += part[0][i];
+            y += part[1][i];
         }
-        if (n_valid) *n_valid = a;
-        if (err_count) *err_count = b;
+        if (n_valid) *n_valid = x;
+        if (err_count) *err_count = y;
     }
-    (void)red;
 }
 
 // ===========================================================================
@@ -81,7 +89,16 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const float *__restri
                                                            const int32_t *n_valid, float *loss) {
     __shared__ BlockRed<kReduceThreads> red;
     double acc = 0.0;
-    for (int64_t r = threadIdx.x; r < T; r += kReduceThreads) acc += (double)loss_rows[r];
+    for (int64_t base = 0; base < T; base += (int64_t)kReduceThreads * kPerThread) {
+        float x[kPerThread];
+#pragma unroll
+        for (int u = 0; u < kPerThread; ++u) {
+            const int64_t r = base + (int64_t)u * kReduceThreads + threadIdx.x;
+            x[u] = (r < T) ? loss_rows[r] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < kPerThread; ++u) acc += (double)x[u];
+    }
     acc = block_sum_d(acc, red, 0);
     if (threadIdx.x == 0) {
         if (reduction == CE_RED_MEAN) acc /= (double)(*n_valid);
@@ -109,7 +126,7 @@ __global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
     __shared__ GradConst gc_sh;
 
     const int tid = threadIdx.x;
-    const int64_t row = blockIdx.x;
+    const int64_t row = xcd_major(blockIdx.x, gridDim.x);
     const int V = (int)a.V;
     const int nvec = V / EPV;
     const int tail0 = nvec * EPV;
@@ -322,7 +339,7 @@ void k_fused_lds(FusedArgs a) {
     __shared__ GradConst gc_sh;
 
     const int tid = threadIdx.x;
-    const int64_t row = blockIdx.x;
+    const int64_t row = xcd_major(blockIdx.x, gridDim.x);
     const int V = (int)a.V;
     const int nvec = V / EPV;
     const int tail0 = nvec * EPV;
@@ -368,7 +385,10 @@ void k_fused_lds(FusedArgs a) {
     }
     const int t = (int)t64;
 
-    // ---- loads: register slots first (needed first), then the LDS part ----
+    // ---- loads: register slots first (needed first), then the LDS part.
+    // While a wave issues memory instructions it runs at raised priority, so
+    // the other workgroup's arithmetic on this CU does not delay the requests.
+    __builtin_amdgcn_s_setprio(1);
     Ch v[NR];
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
@@ -384,6 +404,7 @@ void k_fused_lds(FusedArgs a) {
                                                      16, voff, (NR + q) * TH * 16, 0, kBufNT);
     float ztail = ninf();
     if (tid < ntail) ztail = In::load1(zrow + (tail0 + tid) * In::kSize);
+    __builtin_amdgcn_s_setprio(0);
 
     // ---- target location (wave-uniform tests; see k_fused_resident) ----------
     const int tv = t / EPV;
@@ -501,6 +522,7 @@ void k_fused_lds(FusedArgs a) {
         }
         put(slot, g);
     };
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int i = 0; i < NR; ++i) gradvec(v[i], i);
 #pragma unroll 1
@@ -563,8 +585,9 @@ __global__ __launch_bounds__(THREADS) void k_stats(StatsArgs a) {
     __shared__ BlockRed<THREADS> red;
 
     const int tid = threadIdx.x;
-    const int64_t row = blockIdx.x / a.nchunks;
-    const int ch = (int)(blockIdx.x % a.nchunks);
+    const int64_t unit = xcd_major(blockIdx.x, gridDim.x);
+    const int64_t row = unit / a.nchunks;
+    const int ch = (int)(unit % a.nchunks);
     const int64_t c0 = (int64_t)ch * a.chunk_cols;
     const int64_t c1 = std::min(a.V_local, c0 + a.chunk_cols);
     const int64_t t = a.target[row];
@@ -719,8 +742,9 @@ __global__ __launch_bounds__(THREADS) void k_grad(GradArgs a) {
     __shared__ GradConst gc_sh;
 
     const int tid = threadIdx.x;
-    const int64_t row = blockIdx.x / a.nchunks;
-    const int ch = (int)(blockIdx.x % a.nchunks);
+    const int64_t unit = xcd_major(blockIdx.x, gridDim.x);
+    const int64_t row = unit / a.nchunks;
+    const int ch = (int)(unit % a.nchunks);
     const int64_t c0 = (int64_t)ch * a.chunk_cols;
     const int64_t c1 = std::min(a.V_local, c0 + a.chunk_cols);
     const int64_t nv = (c1 - c0) / EPV;
