@@ -229,8 +229,8 @@ __global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
 #pragma unroll
             for (int i = 0; i < NV; ++i)
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) sd += exp((double)v[i].get(e) - md);
-            sd += exp((double)ztail - md);
+                for (int e = 0; e < EPV; ++e) sd += exp_nonpos((double)v[i].get(e) - md);
+            sd += exp_nonpos((double)ztail - md);
         }
         sd = block_sum_d<THREADS>(sd, red, 0);
         sz = block_sum_d<THREADS>(sz, red, 1);
@@ -566,14 +566,15 @@ struct Online<false> {
 template <>
 struct Online<true> {
     float m = -__builtin_inff();
-    double s = 0.0;
+    double md = -__builtin_inf(), s = 0.0;
     __device__ __forceinline__ void rescale(float vm) {
         if (vm > m) {
-            s = (m == ninf()) ? 0.0 : s * exp((double)m - (double)vm);
+            s = (m == ninf()) ? 0.0 : s * exp_nonpos(md - (double)vm);
             m = vm;
+            md = (double)vm;
         }
     }
-    __device__ __forceinline__ double term(float z) const { return exp((double)z - (double)m); }
+    __device__ __forceinline__ double term(float z) const { return exp_nonpos((double)z - md); }
     __device__ __forceinline__ void add(double t) { s += t; }
     __device__ __forceinline__ MaxSum result() const { return {m, s}; }
 };
@@ -626,6 +627,10 @@ __global__ __launch_bounds__(THREADS) void k_stats(StatsArgs a) {
             else
                 v[u].fill_ninf();
         }
+        // one rescale per UNROLL vectors: the max of the whole group first;
+        // the target test is uniform over the group's column span first
+        const bool t_here = tc >= c0 + base * EPV && tc < c0 + (base + (int64_t)UNROLL * THREADS) * EPV;
+        float vm = ninf();
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int64_t vi = base + (int64_t)u * THREADS + tid;
@@ -640,15 +645,16 @@ __global__ __launch_bounds__(THREADS) void k_stats(StatsArgs a) {
                     for (int e = 0; e < h; ++e) p[e] += p[e + h];
                 sz += (double)p[0];
             }
-            if (tc >= col && tc < col + EPV) v[u].kill((int)(tc - col));
-            float vm = v[u].get(0);
+            if (t_here && tc >= col && tc < col + EPV) v[u].kill((int)(tc - col));
 #pragma unroll
-            for (int e = 1; e < EPV; ++e) vm = fmaxf(vm, v[u].get(e));
-            acc.rescale(vm);
-            if (acc.m != ninf()) {
+            for (int e = 0; e < EPV; ++e) vm = fmaxf(vm, v[u].get(e));
+        }
+        acc.rescale(vm);
+        if (acc.m != ninf()) {
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) acc.add(acc.term(v[u].get(e)));
-            }
         }
     }
     // scalar tail of the chunk
@@ -778,6 +784,7 @@ __global__ __launch_bounds__(THREADS) void k_grad(GradArgs a) {
             const int64_t vi = base + (int64_t)u * THREADS + tid;
             if (vi < nv) v[u].load(zrow + (c0 + vi * EPV) * In::kSize);
         }
+        const bool t_here = tc >= c0 + base * EPV && tc < c0 + (base + (int64_t)UNROLL * THREADS) * EPV;
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int64_t vi = base + (int64_t)u * THREADS + tid;
@@ -786,7 +793,7 @@ __global__ __launch_bounds__(THREADS) void k_grad(GradArgs a) {
             float g[EPV];
 #pragma unroll
             for (int e = 0; e < EPV; ++e) g[e] = grad_elem<OUT, LS>(v[u].get(e), c);
-            if (tc >= col && tc < col + EPV) {
+            if (t_here && tc >= col && tc < col + EPV) {
 #pragma unroll
                 for (int e = 0; e < EPV; ++e)
                     if (col + e == tc) g[e] = c.gk;
