@@ -36,6 +36,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
@@ -43,6 +44,7 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_F64 2 /* logits computed here (the linear classifier below) */
 
 #define ORACLE_RED_NONE 0
 #define ORACLE_RED_SUM 1
@@ -52,6 +54,8 @@
  * IEEE binary32, so widening it is exact; so is float -> double. */
 static double load_elem(const void *base, int dtype, int64_t i)
 {
+    if (dtype == ORACLE_F64)
+        return ((const double *)base)[i];
     if (dtype == ORACLE_F32)
         return (double)((const float *)base)[i];
     uint32_t w = (uint32_t)((const uint16_t *)base)[i] << 16;
@@ -358,6 +362,125 @@ double oracle_reduce(const double *loss, const int32_t *status, int64_t n, int r
     if (reduction == ORACLE_RED_MEAN)
         return total / (double)nv; /* 0/0 = NaN when nothing is valid */
     return total;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exported: cross-entropy of a linear classifier, logits z = E C^T.         */
+/* ------------------------------------------------------------------------ */
+
+/* apple/ml-cross-entropy issue #14 (linear_cross_entropy(embeddings,
+ * classifier weight, labels), and the reference it is checked against there:
+ * logits = embeddings times the transposed classifier, then cross-entropy):
+ * row r's logits are z_rv = sum_d E[r,d] C[v,d] for the V classifier rows;
+ * the loss is the per-row loss above on those logits; by the chain rule the
+ * gradients are dE = G C and dC = G^T E with G = d loss / d z (the rows
+ * oracle_grad writes).  Everything is written out directly in fp64: each
+ * logit is a plain dot product (products of bf16 or fp32 inputs are exact in
+ * fp64), the row statistics and finalize are the ones above, then the two
+ * contractions as plain sums.  E and C share one dtype (bf16, fp32 or fp64;
+ * fp64 inputs serve the finite-difference checks). */
+
+/* z[v] = E_r . C_v for v in [0, V) */
+static void linear_row_logits(const void *E, const void *C, int dtype, int64_t r, int64_t D,
+                              int64_t V, double *z)
+{
+    for (int64_t v = 0; v < V; ++v) {
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; ++d)
+            acc += load_elem(E, dtype, r * D + d) * load_elem(C, dtype, v * D + d);
+        z[v] = acc;
+    }
+}
+
+/* Forward over the n rows of E [n, D] against C [V, D].  Outputs as
+ * oracle_forward (loss, status required; x, lse may be NULL). */
+void oracle_linear_forward(const void *E, const void *C, int dtype, int64_t n, int64_t D,
+                           int64_t V, const int64_t *target, int64_t ignore_index, double eps,
+                           double *loss, int32_t *status, double *x_out, double *lse_out)
+{
+#pragma omp parallel
+    {
+        double *z = (double *)malloc((size_t)V * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < n; ++r) {
+            const int64_t t = target[r];
+            row_final f = {0, 0, 0, 0};
+            int32_t st;
+            if (t == ignore_index) {
+                st = 0;
+            } else if (t < 0 || t >= V) {
+                st = -1;
+                f.loss = NAN;
+            } else {
+                double m, s, zt, sz;
+                int32_t own;
+                linear_row_logits(E, C, dtype, r, D, V, z);
+                shard_row_stats(z, ORACLE_F64, V, t, &m, &s, &zt, &own, &sz);
+                finalize_row(m, s, zt, sz, V, eps, &f);
+                st = 1;
+            }
+            loss[r] = f.loss;
+            status[r] = st;
+            if (x_out) x_out[r] = f.x;
+            if (lse_out) lse_out[r] = f.lse;
+        }
+        free(z);
+    }
+}
+
+/* Gradients, from the status, x and lse oracle_linear_forward returned and
+ * the per-row scale k:
+ *   G [n, V]  d loss_r / d z_rv times k_r (written; +0 on rows whose status
+ *             is not 1), the same formula as oracle_grad;
+ *   dE [n, D] = G C            (may be NULL)
+ *   dC [V, D] = G^T E          (may be NULL)
+ *   rsE [n, D] = sqrt(sum_v (G[r,v] C[v,d])^2),
+ *   rsC [V, D] = sqrt(sum_r (G[r,v] E[r,d])^2)   (may be NULL): the scales of
+ *             the rounding error a bf16 copy of G brings into each sum. */
+void oracle_linear_backward(const void *E, const void *C, int dtype, int64_t n, int64_t D,
+                            int64_t V, const int64_t *target, const int32_t *status,
+                            const double *x, const double *lse, double eps, const double *k,
+                            double *G, double *dE, double *dC, double *rsE, double *rsC)
+{
+    const double u = eps / (double)V;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r) {
+        double *g = G + (size_t)r * (size_t)V;
+        if (status[r] != 1) {
+            for (int64_t v = 0; v < V; ++v)
+                g[v] = 0.0;
+        } else {
+            linear_row_logits(E, C, dtype, r, D, V, g);
+            for (int64_t v = 0; v < V; ++v)
+                g[v] = k[r] * (exp(g[v] - lse[r]) - u);
+            g[target[r]] = k[r] * (-sigmoid(x[r]) + eps * (double)(V - 1) / (double)V);
+        }
+        for (int64_t d = 0; d < D && (dE || rsE); ++d) {
+            double acc = 0.0, sq = 0.0;
+            for (int64_t v = 0; v < V; ++v) {
+                const double p = g[v] * load_elem(C, dtype, v * D + d);
+                acc += p;
+                sq += p * p;
+            }
+            if (dE) dE[r * D + d] = acc;
+            if (rsE) rsE[r * D + d] = sqrt(sq);
+        }
+    }
+    if (!dC && !rsC)
+        return;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t v = 0; v < V; ++v) {
+        for (int64_t d = 0; d < D; ++d) {
+            double acc = 0.0, sq = 0.0;
+            for (int64_t r = 0; r < n; ++r) {
+                const double p = G[(size_t)r * (size_t)V + v] * load_elem(E, dtype, r * D + d);
+                acc += p;
+                sq += p * p;
+            }
+            if (dC) dC[v * D + d] = acc;
+            if (rsC) rsC[v * D + d] = sqrt(sq);
+        }
+    }
 }
 
 /* ------------------------------------------------------------------------ */

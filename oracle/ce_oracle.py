@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(HERE, "libce_oracle.so")
 
 F32 = 0
 BF16 = 1
+F64 = 2
 RED_NONE, RED_SUM, RED_MEAN = 0, 1, 2
 _RED = {"none": RED_NONE, "sum": RED_SUM, "mean": RED_MEAN}
 
@@ -53,6 +54,11 @@ def _load():
         lib.oracle_reduce.restype = d
         lib.oracle_to_bf16.argtypes = [P, i64, P]
         lib.oracle_to_bf16.restype = None
+        lib.oracle_linear_forward.argtypes = [P, P, i, i64, i64, i64, P, i64, d, P, P, P, P]
+        lib.oracle_linear_forward.restype = None
+        lib.oracle_linear_backward.argtypes = [P, P, i, i64, i64, i64, P, P, P, P, d, P,
+                                               P, P, P, P, P]
+        lib.oracle_linear_backward.restype = None
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = i
         _lib = lib
@@ -180,6 +186,59 @@ def fwd_bwd(z, target, *, ignore_index=-100, eps=0.0, reduction="mean", grad_out
     g = grad(z, target, f, k, eps=eps)
     return {"loss": loss, "loss_rows": f["loss"], "status": f["status"], "n_valid": nv,
             "n_bad": nb, "grad": g, "fwd": f, "k": k}
+
+
+def _matrix_args(a):
+    if a.ndim != 2:
+        raise ValueError("expected a 2-D matrix")
+    a = np.ascontiguousarray(a)
+    code = {np.dtype(np.uint16): BF16, np.dtype(np.float32): F32,
+            np.dtype(np.float64): F64}.get(a.dtype)
+    if code is None:
+        raise TypeError("matrix must be uint16 (bf16 bits), float32 or float64")
+    return a, code
+
+
+def linear_fwd_bwd(E, C, target, *, ignore_index=-100, eps=0.0, reduction="mean",
+                   grad_output=1.0, n_valid=None, grads=True, dC=True, scales=True):
+    """Cross-entropy of the logits E C^T (apple/ml-cross-entropy issue #14,
+    linear_cross_entropy): E [n, D] and C [V, D] of one dtype (bf16 bits as
+    uint16, float32 or float64).  Returns loss, loss_rows, status, n_valid,
+    lse, and with ``grads`` the fp64 G [n, V], dE [n, D], dC [V, D] (unless
+    ``dC`` is False) and the root-sum-square scales rsE, rsC (with
+    ``scales``).  ``n_valid`` overrides the mean's denominator when E holds a
+    sample of the rows of a larger batch."""
+    E, code = _matrix_args(E)
+    C, code_c = _matrix_args(C)
+    if code != code_c or E.shape[1] != C.shape[1]:
+        raise ValueError("E and C must share dtype and hidden size")
+    n, D = E.shape
+    V = C.shape[0]
+    target = _i64(target)
+    assert target.shape == (n,)
+    lib = _load()
+    loss_rows = np.zeros(n, np.float64)
+    status = np.zeros(n, np.int32)
+    x = np.zeros(n, np.float64)
+    lse = np.zeros(n, np.float64)
+    lib.oracle_linear_forward(_ptr(E), _ptr(C), code, n, D, V, _ptr(target), int(ignore_index),
+                              float(eps), _ptr(loss_rows), _ptr(status), _ptr(x), _ptr(lse))
+    loss, nv, nb = reduce(loss_rows, status, reduction)
+    out = {"loss": loss, "loss_rows": loss_rows, "status": status, "n_valid": nv, "n_bad": nb,
+           "x": x, "lse": lse}
+    if not grads:
+        return out
+    k = row_scale(status, reduction, grad_output, nv if n_valid is None else n_valid)
+    G = np.empty((n, V), np.float64)
+    dE = np.empty((n, D), np.float64)
+    dCo = np.empty((V, D), np.float64) if dC else None
+    rsE = np.empty((n, D), np.float64) if scales else None
+    rsC = np.empty((V, D), np.float64) if (scales and dC) else None
+    lib.oracle_linear_backward(_ptr(E), _ptr(C), code, n, D, V, _ptr(target), _ptr(status),
+                               _ptr(x), _ptr(lse), float(eps), _ptr(np.ascontiguousarray(k)),
+                               _ptr(G), _ptr(dE), _ptr(dCo), _ptr(rsE), _ptr(rsC))
+    out.update(G=G, dE=dE, dC=dCo, rsE=rsE, rsC=rsC, k=k)
+    return out
 
 
 def to_bf16(v):

@@ -1,0 +1,142 @@
+"""Pins of the oracle's linear-classifier cross-entropy (logits z = E C^T,
+apple/ml-cross-entropy issue #14, linear_cross_entropy) to facts outside
+itself, no GPU needed: a closed form at C = 0, central finite differences in
+fp64, torch's float64 autograd through matmul + cross_entropy on the CPU,
+numpy's matmul for the two contractions, and the zero column sums of dC.
+A transposed operand, a dropped scale, a wrong smoothing weight or a G row
+that does not sum to zero fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ce_oracle as O
+
+
+def _case(n=6, D=5, V=9, seed=0, scale=0.7):
+    rng = np.random.default_rng(seed)
+    E = rng.standard_normal((n, D))
+    C = rng.standard_normal((V, D)) * scale
+    t = rng.integers(0, V, n)
+    t[1] = -100
+    return E, C, t
+
+
+@pytest.mark.parametrize("eps", [0.0, 0.1])
+def test_zero_classifier_closed_form(eps):
+    """C = 0: every row is uniform, so loss_r = log V, dE = 0 and
+    dC[v] = sum_r k (1 - eps) (1/V - [t_r = v]) E_r."""
+    E, _, t = _case()
+    V = 9
+    C = np.zeros((V, E.shape[1]))
+    o = O.linear_fwd_bwd(E, C, t, eps=eps, reduction="sum")
+    valid = t != -100
+    assert np.allclose(o["loss_rows"][valid], math.log(V), rtol=1e-14, atol=0)
+    assert np.all(o["loss_rows"][~valid] == 0.0)
+    assert np.all(o["dE"] == 0.0)
+    want = np.zeros((V, E.shape[1]))
+    for r in np.nonzero(valid)[0]:
+        for v in range(V):
+            want[v] += (1.0 - eps) * ((1.0 / V) - (1.0 if v == t[r] else 0.0)) * E[r]
+    assert np.allclose(o["dC"], want, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("reduction", ["sum", "mean", "none"])
+@pytest.mark.parametrize("eps", [0.0, 0.2])
+def test_matches_torch_float64_autograd(reduction, eps):
+    """Loss and both gradients against torch's float64 matmul + cross_entropy
+    and its autograd (CPU), with a grad_output that is not 1."""
+    E, C, t = _case(n=7, D=6, V=11, seed=3)
+    go = 0.75 if reduction != "none" else np.linspace(0.5, 1.5, 7)
+    o = O.linear_fwd_bwd(E, C, t, eps=eps, reduction=reduction, grad_output=go)
+    Et = torch.tensor(E, requires_grad=True)
+    Ct = torch.tensor(C, requires_grad=True)
+    loss = torch.nn.functional.cross_entropy(Et @ Ct.T, torch.tensor(t), ignore_index=-100,
+                                             label_smoothing=eps, reduction=reduction)
+    loss.backward(torch.tensor(go, dtype=torch.float64))
+    if reduction == "none":
+        assert np.allclose(o["loss_rows"], loss.detach().numpy(), rtol=1e-13, atol=1e-15)
+    else:
+        assert abs(o["loss"] - loss.item()) <= 1e-13 * abs(loss.item())
+    assert np.allclose(o["dE"], Et.grad.numpy(), rtol=1e-11, atol=1e-14)
+    assert np.allclose(o["dC"], Ct.grad.numpy(), rtol=1e-11, atol=1e-14)
+
+
+@pytest.mark.parametrize("eps", [0.0, 0.1])
+def test_central_finite_differences(eps):
+    """d(sum of losses)/dE and /dC against central differences in fp64."""
+    E, C, t = _case(n=4, D=3, V=5, seed=5)
+    o = O.linear_fwd_bwd(E, C, t, eps=eps, reduction="sum")
+    h = 1e-6
+
+    def total(E_, C_):
+        return O.linear_fwd_bwd(E_, C_, t, eps=eps, reduction="sum", grads=False)["loss"]
+
+    for (r, d) in [(0, 0), (2, 1), (3, 2)]:
+        Ep, Em = E.copy(), E.copy()
+        Ep[r, d] += h
+        Em[r, d] -= h
+        fd = (total(Ep, C) - total(Em, C)) / (2 * h)
+        assert abs(fd - o["dE"][r, d]) <= 1e-7 * max(1.0, abs(fd))
+    for (v, d) in [(0, 0), (int(t[0]), 2), (4, 1)]:
+        Cp, Cm = C.copy(), C.copy()
+        Cp[v, d] += h
+        Cm[v, d] -= h
+        fd = (total(E, Cp) - total(E, Cm)) / (2 * h)
+        assert abs(fd - o["dC"][v, d]) <= 1e-7 * max(1.0, abs(fd))
+
+
+def test_agrees_with_stored_logits_oracle():
+    """The logits E C^T formed by numpy's matmul and rounded to fp32, fed to
+    the stored-logits oracle, give the same per-row loss as the linear
+    oracle up to the fp32 rounding of the logits."""
+    E, C, t = _case(n=8, D=16, V=40, seed=7)
+    o = O.linear_fwd_bwd(E, C, t, grads=False)
+    z = (E @ C.T).astype(np.float32)
+    f = O.forward(z, t)
+    v = f["status"] == 1
+    assert np.array_equal(f["status"], o["status"])
+    assert np.allclose(o["loss_rows"][v], f["loss"][v], rtol=1e-5)
+
+
+def test_contractions_and_scales_match_numpy():
+    """dE = G C, dC = G^T E, rsE = sqrt(G^2 C^2), rsC = sqrt((G^2)^T E^2)
+    with numpy's matmul on the oracle's own G; dC's columns sum to zero."""
+    E, C, t = _case(n=9, D=7, V=13, seed=11)
+    o = O.linear_fwd_bwd(E, C, t, eps=0.1)
+    G = o["G"]
+    assert np.allclose(o["dE"], G @ C, rtol=1e-12, atol=1e-15)
+    assert np.allclose(o["dC"], G.T @ E, rtol=1e-12, atol=1e-15)
+    assert np.allclose(o["rsE"], np.sqrt((G * G) @ (C * C)), rtol=1e-12, atol=1e-15)
+    assert np.allclose(o["rsC"], np.sqrt((G * G).T @ (E * E)), rtol=1e-12, atol=1e-15)
+    colsum = o["dC"].sum(axis=0)
+    assert np.all(np.abs(colsum) <= 1e-14 * np.abs(o["dC"]).sum(axis=0) + 1e-16)
+    assert np.allclose(G.sum(axis=1), 0.0, atol=1e-15)
+
+
+def test_bf16_inputs_are_decoded_exactly():
+    """bf16 bit patterns give the same results as their exact fp64 values."""
+    E, C, t = _case(n=5, D=8, V=10, seed=13)
+    Eb, Cb = O.to_bf16(E), O.to_bf16(C)
+    a = O.linear_fwd_bwd(Eb, Cb, t, eps=0.1)
+    b = O.linear_fwd_bwd(O.bf16_to_f64(Eb), O.bf16_to_f64(Cb), t, eps=0.1)
+    for key in ("loss_rows", "dE", "dC", "rsE"):
+        assert np.array_equal(a[key], b[key])
+
+
+def test_ignored_and_bad_rows():
+    """Ignored rows: loss +0, G row +0, no contribution to dC; a target
+    outside [0, V) is status -1 and NaN loss."""
+    E, C, t = _case(n=6, D=4, V=7, seed=17)
+    t = t.copy()
+    t[3] = 7
+    o = O.linear_fwd_bwd(E, C, t, reduction="sum")
+    assert o["status"][1] == 0 and o["loss_rows"][1] == 0.0
+    assert o["status"][3] == -1 and math.isnan(o["loss_rows"][3])
+    assert np.all(o["G"][1] == 0.0) and np.all(o["G"][3] == 0.0)
+    assert np.all(o["dE"][1] == 0.0) and np.all(o["dE"][3] == 0.0)
+    keep = [r for r in range(6) if r not in (1, 3)]
+    o2 = O.linear_fwd_bwd(E[keep], C, t[keep], reduction="sum")
+    assert np.allclose(o["dC"], o2["dC"], rtol=1e-13, atol=1e-16)
