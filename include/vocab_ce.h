@@ -209,6 +209,68 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
                      int grad_dtype, int64_t ldg, void *ws, size_t ws_bytes,
                      void *stream);
 
+/* ------------------------------------------------------------------------ */
+/* Cross-entropy of a linear classifier, logits = E C^T never stored.        */
+/* ------------------------------------------------------------------------ */
+
+/* apple/ml-cross-entropy issue #14: linear_cross_entropy(embeddings,
+ * classifier weight, labels) fuses the classifier product with the loss so
+ * that the [N, V] logits are never materialised; the thread's fix keeps the
+ * dC and dE accumulations out of low precision (fp32 accumulators, optional
+ * Kahan compensation: use_kahan, impl="cce_exact", which also turns off
+ * gradient filtering -- no filtering is done here).
+ *
+ *   z_rv = sum_d E[r,d] C[v,d]     (bf16 inputs, fp32 accumulation, MFMA)
+ *   loss_r, the 1/4 target select, ignore_index, label smoothing and the
+ *   row scale k_r exactly as for ce_fused_fwd_bwd on those logits;
+ *   G = k (softmax(z) - q), rounded to bf16 (round-to-nearest-even) as the
+ *   operand of the two backward products;
+ *   dE = G C   [N, D] fp32,  dC = G^T E  [V, D] fp32.
+ *
+ * The vocabulary is processed in chunks of CE_LINEAR_CHUNK classes: dC rows
+ * of a chunk are complete after it, dE is summed over the chunks in fp32 or,
+ * with CE_ACC_KAHAN, with a Kahan compensation term (one more [N, D] fp32
+ * workspace buffer).  Everything is deterministic (no atomics). */
+#define CE_LINEAR_CHUNK 8192
+
+typedef enum {
+    CE_ACC_FP32 = 0, /* dE summed over vocabulary chunks in fp32 */
+    CE_ACC_KAHAN = 1 /* ... with Kahan compensation */
+} ce_accum;
+
+typedef struct {
+    int64_t N;            /* rows of E (tokens) */
+    int64_t D;            /* hidden size: columns of E and C; a multiple of 8 */
+    int64_t V;            /* classes: rows of C */
+    int64_t ignore_index; /* target value that marks an ignored row */
+    float label_smoothing;/* eps in [0, 1) */
+    int32_t reduction;    /* ce_reduction */
+    int32_t accum;        /* ce_accum */
+    int32_t reserved;     /* 0 */
+} ce_linear_problem;
+
+/* Workspace bytes ce_linear_fwd_bwd needs; `backward` = 0 when dE and dC
+ * are both NULL (loss only).  Host function; 0 for an invalid problem. */
+size_t ce_linear_workspace_bytes(const ce_linear_problem *prob, int backward);
+
+/* Loss and, if dE or dC is non-NULL, both gradients.
+ *   E [N, D] bf16, row-major, row stride D; C [V, D] bf16, row stride D;
+ *   both 16-byte aligned.
+ *   target [N] int64.
+ *   grad_output: as in ce_backward (device; NULL means 1).
+ *   loss_rows [N], loss [1], n_valid [1], err_count [1]: optional outputs
+ *   as in ce_fused_fwd_bwd.
+ *   dE [N, D] fp32 and dC [V, D] fp32, row-major: either both or neither.
+ *   ws/ws_bytes: at least ce_linear_workspace_bytes(prob, dE != NULL).
+ * Errors: CE_ERR_NULL (E, C or target NULL, or only one of dE and dC),
+ * CE_ERR_SHAPE (N < 0, D < 8 or not a multiple of 8, V < 1, sizes beyond
+ * the kernels' 32-bit block offsets), CE_ERR_SMOOTHING, CE_ERR_REDUCTION,
+ * CE_ERR_ARG (unknown accum), CE_ERR_WORKSPACE, CE_ERR_HIP. */
+int ce_linear_fwd_bwd(const ce_linear_problem *prob, const void *E, const void *C,
+                      const int64_t *target, const float *grad_output, float *loss_rows,
+                      float *loss, int32_t *n_valid, int32_t *err_count, float *dE, float *dC,
+                      void *ws, size_t ws_bytes, void *stream);
+
 /* Human-readable name of a ce_status.  Host function, static storage. */
 const char *ce_status_str(int status);
 

@@ -123,3 +123,58 @@ def to_numpy_logits(x: torch.Tensor) -> np.ndarray:
     if x.dtype == torch.float32:
         return x.numpy()
     raise TypeError(f"unsupported logits dtype {x.dtype}")
+
+
+# ---------------------------------------------------------------------------
+# Linear-classifier workloads (embeddings E [N, D], classifier C [V, D]).
+# ---------------------------------------------------------------------------
+
+@dataclass
+class LinearCase:
+    """Recipe (draws from one ``torch.Generator`` seeded with ``seed``, in
+    this order): E ~ N(0, sigma_e^2) and C ~ N(0, sigma_c^2), both drawn in
+    fp32 row blocks and rounded to bf16 (RNE); targets ~ uniform integers in
+    [0, V); a random permutation of the rows whose first ``n_ignored`` get
+    ``ignore_index``.  With sigma_e = 1 and sigma_c = 0.02 the logits have
+    standard deviation about 0.02 sqrt(D) (0.905 at D = 2048)."""
+    name: str
+    N: int
+    D: int
+    V: int
+    sigma_e: float
+    sigma_c: float
+    n_ignored: int
+    seed: int
+    ignore_index: int = -100
+    eps: float = 0.0
+    reduction: str = "mean"
+
+
+# The fused linear-classifier workload (embeddings [8192, 2048], classifier
+# [128256, 2048], 1% of rows ignored), and the toy shape of
+# apple/ml-cross-entropy issue #14 (8191 shifted rows of a 128-wide
+# embedding, 32 classes).
+LINEAR = LinearCase("linear", 8192, 2048, 128256, 1.0, 0.02, 82, 1005)
+CCE_TOY = LinearCase("cce_toy", 8191, 128, 32, 1.0, 0.1, 0, 1006)
+
+
+def generate_linear(case: LinearCase, device="cpu", block_rows: int = 4096):
+    """Draw (E [N, D] bf16, C [V, D] bf16, target [N] int64) on ``device``."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(case.seed)
+
+    def draw(rows, sigma):
+        out = torch.empty((rows, case.D), dtype=torch.bfloat16, device=dev)
+        for r0 in range(0, rows, block_rows):
+            r1 = min(rows, r0 + block_rows)
+            blk = torch.randn((r1 - r0, case.D), generator=g, device=dev, dtype=torch.float32)
+            out[r0:r1].copy_(blk.mul_(sigma))
+        return out
+
+    E = draw(case.N, case.sigma_e)
+    C = draw(case.V, case.sigma_c)
+    target = torch.randint(0, case.V, (case.N,), generator=g, device=dev, dtype=torch.int64)
+    perm = torch.randperm(case.N, generator=g, device=dev)
+    target[perm[:case.n_ignored]] = case.ignore_index
+    return E, C, target

@@ -118,3 +118,48 @@ def collapse_rows(logits, target, margin=15.0, ignore_index=-100):
         if zt - row.max().item() > margin:
             out.append(i)
     return out
+
+
+# --------------------------------------------------------------------------
+# linear classifier (logits E C^T)
+# --------------------------------------------------------------------------
+# The backward products take G = k (softmax - q) rounded once to bf16, as the
+# matrix-core operand; each element's rounding error is at most 2^-8 of it
+# (half a bf16 ulp) and about 2^-7.5 / sqrt(12) = 1.6e-3 of it in rms.  A
+# gradient entry sum_v G_v C_v then carries an error of rms about
+# 1.6e-3 * rs, rs = sqrt(sum_v (G_v C_v)^2) (the oracle's rsE / rsC).  The
+# checks: every entry within 2^-6 rs (about 10 rms), and the whole matrix
+# within 4e-3 in the rs-weighted Frobenius norm (2.5x the expected 1.6e-3,
+# which a 1% scale or sign slip in any term exceeds).  fp32 accumulation and
+# the fp32 logits add about 1e-5 of rs and are inside both bounds.
+LIN_ELEM_TOL = 2.0 ** -6
+LIN_FROB_TOL = 4e-3
+
+
+def assert_linear_grad_close(gpu, ref, rs, what=""):
+    g = gpu.detach().to("cpu").double().numpy()
+    assert np.all(np.isfinite(g)), f"{what}: non-finite gradient"
+    d = np.abs(g - ref)
+    bad = d > LIN_ELEM_TOL * rs + 1e-30
+    assert not bad.any(), (f"{what}: {int(bad.sum())} entries beyond 2^-6 rs; worst "
+                           f"{float((d / np.maximum(rs, 1e-300)).max()):.3e} rs")
+    den = float(np.sqrt((rs * rs).sum()))
+    if den > 0:
+        fro = float(np.sqrt((d * d).sum())) / den
+        assert fro <= LIN_FROB_TOL, f"{what}: Frobenius error {fro:.3e} of rs"
+
+
+def linear_oracle_for(E, C, target, *, ignore_index=-100, eps=0.0, reduction="mean",
+                      grad_output=1.0, n_valid=None, dC=True):
+    """The linear-classifier oracle on exactly the bytes the GPU consumed."""
+    eps = float(np.float32(eps))
+    Eb = E.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
+    Cb = C.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
+    t = target.detach().to("cpu").numpy()
+    go = grad_output
+    if isinstance(go, torch.Tensor):
+        go = go.detach().to("cpu").double().numpy()
+        if reduction != "none":
+            go = float(go.reshape(-1)[0])
+    return O.linear_fwd_bwd(Eb, Cb, t, ignore_index=ignore_index, eps=eps, reduction=reduction,
+                            grad_output=go, n_valid=n_valid, dC=dC)

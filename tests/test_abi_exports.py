@@ -82,3 +82,51 @@ def test_null_and_dtype_checks(lib):
     one = ctypes.c_void_p(16)
     assert lib.ce_forward(ctypes.byref(shard), one, 1, one, one, None, one, None, None, None,
                           None, 0, None) == -10
+
+
+def test_linear_problem_struct_and_workspace(lib):
+    assert ctypes.sizeof(B.CELinearProblem) == 48
+    p = B.make_linear_problem(8192, 2048, 128256)
+    fwd = B.ce_linear_workspace_bytes(p, 0)
+    both = B.ce_linear_workspace_bytes(p, 1)
+    # forward: fragment-major E and C, per-(256-class tile, row) statistics
+    assert fwd >= (8192 + 128256) * 2048 * 2 + 501 * 8192 * 32
+    # backward adds the transposed operands and one chunk of G and G^T
+    assert both >= fwd + (8192 + 128256) * 2048 * 2 + 2 * 8192 * B.CE_LINEAR_CHUNK * 2
+    k = B.make_linear_problem(8192, 2048, 128256, accum="kahan")
+    assert B.ce_linear_workspace_bytes(k, 1) >= both + 8192 * 2048 * 4
+    assert B.ce_linear_workspace_bytes(B.make_linear_problem(4, 12, 10), 0) == 0  # D % 8
+    assert B.ce_linear_workspace_bytes(B.make_linear_problem(4, 16, 10, accum=5), 0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=12), -2), (dict(D=0), -2), (dict(V=0), -2), (dict(N=-1), -2),
+    (dict(label_smoothing=1.0), -3), (dict(reduction=9), -5), (dict(accum=3), -10),
+])
+def test_linear_argument_checks_before_any_launch(lib, kw, status):
+    args = dict(N=4, D=16, V=10)
+    args.update({k: v for k, v in kw.items() if k in args})
+    p = B.make_linear_problem(args["N"], args["D"], args["V"],
+                              **{k: v for k, v in kw.items() if k not in args})
+    one = ctypes.c_void_p(256)
+    rc = lib.ce_linear_fwd_bwd(ctypes.byref(p), one, one, one, None, None, None, None, None,
+                               None, None, one, 1 << 40, None)
+    assert rc == status
+
+
+def test_linear_null_and_pairing_checks(lib):
+    p = B.make_linear_problem(4, 16, 10)
+    one = ctypes.c_void_p(256)
+    ws = B.ce_linear_workspace_bytes(p, 1)
+    # E missing
+    assert lib.ce_linear_fwd_bwd(ctypes.byref(p), None, one, one, None, None, None, None, None,
+                                 None, None, one, ws, None) == -1
+    # dE without dC
+    assert lib.ce_linear_fwd_bwd(ctypes.byref(p), one, one, one, None, None, None, None, None,
+                                 one, None, one, ws, None) == -1
+    # workspace too small
+    assert lib.ce_linear_fwd_bwd(ctypes.byref(p), one, one, one, None, None, None, None, None,
+                                 None, None, one, 16, None) == -6
+    # misaligned E
+    assert lib.ce_linear_fwd_bwd(ctypes.byref(p), ctypes.c_void_p(258), one, one, None, None,
+                                 None, None, None, None, None, one, ws, None) == -2

@@ -1,0 +1,168 @@
+"""GPU parity of the linear-classifier cross-entropy (ce_linear_fwd_bwd)
+against the fp64 oracle, through the C ABI.
+
+Loss: every valid row within 1e-5 relative (ignored rows exactly +0, bad
+targets NaN), the reduced loss within 1e-5.  dE and dC: the bound of
+``parity_util.assert_linear_grad_close`` (G is a bf16 operand of the
+backward products).  Shapes cover padding in every dimension (tokens not a
+multiple of 256, hidden size not a multiple of 64, classes not a multiple
+of 256), several vocabulary chunks with a ragged last one, both dE
+accumulation modes, label smoothing, every reduction, the toy shape of
+apple/ml-cross-entropy issue #14, and the full 8192 x 2048 x 128256
+workload (sampled rows; full gradients at 16 rows of the full width).
+"""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import vocab_softmax_cross_row_amd as vce
+from synth import ce_inputs as S
+from tests.parity_util import (LOSS_RTOL, assert_linear_grad_close, assert_loss_rows,
+                               assert_scalar_loss, linear_oracle_for)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _case(N, D, V, seed, n_ignored=None, **kw):
+    base = S.LINEAR
+    if n_ignored is None:
+        n_ignored = max(1, round(N * base.n_ignored / base.N))
+    return dataclasses.replace(base, name=f"lin_{N}x{D}x{V}", N=N, D=D, V=V, seed=seed,
+                               n_ignored=n_ignored, **kw)
+
+
+def _run(case, *, accum="fp32", grad_output=None, backward=True):
+    print(f"[linear] {case.name} eps={case.eps} red={case.reduction} accum={accum}", flush=True)
+    E, C, t = S.generate_linear(case, device=DEV)
+    go = grad_output
+    out = vce.linear_cross_entropy(E, C, t, ignore_index=case.ignore_index,
+                                   label_smoothing=case.eps, reduction=case.reduction,
+                                   grad_output=go, backward=backward, accum=accum)
+    torch.cuda.synchronize()
+    return E, C, t, out
+
+
+def _check(case, E, C, t, out, grad_output=1.0, what=""):
+    ref = linear_oracle_for(E, C, t, ignore_index=case.ignore_index, eps=case.eps,
+                            reduction=case.reduction, grad_output=grad_output)
+    assert_loss_rows(out["loss_rows"], {"loss_rows": ref["loss_rows"], "status": ref["status"]},
+                     what)
+    if case.reduction != "none":
+        assert_scalar_loss(out["loss"].item(), ref["loss"], what)
+    assert int(out["n_valid"].item()) == ref["n_valid"]
+    assert int(out["err_count"].item()) == ref["n_bad"]
+    if out["dE"] is not None:
+        assert_linear_grad_close(out["dE"], ref["dE"], ref["rsE"], what + " dE")
+        assert_linear_grad_close(out["dC"], ref["dC"], ref["rsC"], what + " dC")
+    return ref
+
+
+def test_ragged_in_every_dimension():
+    case = _case(300, 72, 1000, 2101)
+    E, C, t, out = _run(case)
+    _check(case, E, C, t, out, what="300x72x1000")
+
+
+@pytest.mark.parametrize("accum", ["fp32", "kahan"])
+def test_several_chunks_with_smoothing(accum):
+    # 2 vocabulary chunks, the second ragged; sum with a grad_output of 0.5
+    case = _case(512, 256, 8192 + 300, 2102, eps=0.1, reduction="sum")
+    go = torch.tensor([0.5], device=DEV)
+    E, C, t, out = _run(case, accum=accum, grad_output=go)
+    _check(case, E, C, t, out, grad_output=go, what=f"chunks {accum}")
+
+
+def test_reduction_none_per_row_grad_output():
+    case = _case(260, 64, 700, 2103, reduction="none")
+    go = torch.linspace(0.25, 2.0, 260, device=DEV)
+    E, C, t, out = _run(case, grad_output=go)
+    _check(case, E, C, t, out, grad_output=go, what="none")
+
+
+def test_cce_issue_toy_shape():
+    # apple/ml-cross-entropy issue #14: 8191 shifted rows, hidden 128, 32 classes
+    case = dataclasses.replace(S.CCE_TOY)
+    E, C, t, out = _run(case)
+    _check(case, E, C, t, out, what="cce toy")
+
+
+def test_kahan_and_fp32_agree_closely():
+    case = _case(256, 128, 3 * 8192, 2104)
+    E, C, t, a = _run(case, accum="fp32")
+    b = vce.linear_cross_entropy(E, C, t, accum="kahan")
+    torch.cuda.synchronize()
+    assert torch.equal(a["dC"], b["dC"])          # dC rows are complete in one chunk
+    assert torch.equal(a["loss_rows"], b["loss_rows"])
+    d = (a["dE"] - b["dE"]).abs().max().item()
+    assert d <= 1e-6 * b["dE"].abs().max().item()
+
+
+def test_loss_only_matches_backward_call():
+    case = _case(300, 72, 1000, 2105)
+    E, C, t, out = _run(case, backward=False)
+    assert out["dE"] is None and out["dC"] is None
+    _, _, _, full = _run(case)
+    assert torch.equal(out["loss_rows"], full["loss_rows"])
+    assert torch.equal(out["loss"], full["loss"])
+
+
+def test_bad_targets_and_all_ignored():
+    case = _case(200, 64, 500, 2106)
+    E, C, t = S.generate_linear(case, device=DEV)
+    t = t.clone()
+    t[3] = 500          # out of range
+    t[7] = -5
+    out = vce.linear_cross_entropy(E, C, t)
+    torch.cuda.synchronize()
+    ref = _check(case, E, C, t, out, what="bad targets")
+    assert ref["n_bad"] == 2 and int(out["err_count"].item()) == 2
+    assert math.isnan(out["loss"].item())
+    t_all = torch.full_like(t, -100)
+    out = vce.linear_cross_entropy(E, C, t_all)
+    torch.cuda.synchronize()
+    assert math.isnan(out["loss"].item()) and int(out["n_valid"].item()) == 0
+    assert torch.all(out["dE"] == 0) and torch.all(out["dC"] == 0)
+
+
+def test_deterministic():
+    case = _case(300, 136, 2000, 2107)
+    E, C, t, a = _run(case)
+    b = vce.linear_cross_entropy(E, C, t)
+    torch.cuda.synchronize()
+    for k in ("loss_rows", "dE", "dC"):
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_full_width_sixteen_rows():
+    # the full hidden size and vocabulary, in the launch configuration of the
+    # full workload, at 16 rows: full dE and dC parity
+    case = dataclasses.replace(S.LINEAR, name="linear_16rows", N=16, n_ignored=1)
+    E, C, t, out = _run(case)
+    _check(case, E, C, t, out, what="16 x 2048 x 128256")
+
+
+def test_full_workload_sampled_rows():
+    case = S.LINEAR
+    E, C, t, out = _run(case)
+    n_valid = int((t != case.ignore_index).sum().item())
+    assert int(out["n_valid"].item()) == n_valid
+    g = torch.Generator().manual_seed(7)
+    rows = torch.randperm(case.N, generator=g)[:8].tolist()
+    rows[0] = int(torch.nonzero(t.cpu() == case.ignore_index)[0, 0])  # one ignored row
+    ref = linear_oracle_for(E[rows], C, t[rows], n_valid=n_valid, dC=False)
+    sel = torch.tensor(rows)
+    assert_loss_rows(out["loss_rows"].cpu()[sel], {"loss_rows": ref["loss_rows"],
+                                                   "status": ref["status"]}, "sampled")
+    assert_linear_grad_close(out["dE"].cpu()[sel], ref["dE"], ref["rsE"], "sampled dE")
+    # the mean over all rows agrees with the per-row losses it is made of
+    lr = out["loss_rows"].double()
+    assert abs(out["loss"].item() - lr.sum().item() / n_valid) <= LOSS_RTOL * abs(out["loss"].item())
+    assert torch.isfinite(out["dC"]).all()
+    # every class row of dC is a sum over the valid tokens of G E: with logits
+    # of spread about 0.9 every class has gradient mass, so no row is zero
+    assert (out["dC"].abs().sum(dim=1) > 0).all()

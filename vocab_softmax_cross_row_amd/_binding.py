@@ -27,7 +27,11 @@ REDUCTIONS = {"none": CE_RED_NONE, "sum": CE_RED_SUM, "mean": CE_RED_MEAN}
 
 # symbols declared in include/vocab_ce.h
 EXPORTS = ("ce_workspace_bytes", "ce_forward", "ce_merge_shard_stats", "ce_backward",
-           "ce_fused_fwd_bwd", "ce_status_str", "ce_version")
+           "ce_fused_fwd_bwd", "ce_linear_workspace_bytes", "ce_linear_fwd_bwd",
+           "ce_status_str", "ce_version")
+CE_ACC_FP32, CE_ACC_KAHAN = 0, 1
+ACCUMS = {"fp32": CE_ACC_FP32, "kahan": CE_ACC_KAHAN}
+CE_LINEAR_CHUNK = 8192
 
 # device structs, as numpy dtypes for reading them back
 ROW_STATS_DTYPE = np.dtype([("m", "<f4"), ("zt", "<f4"), ("own", "<i4"), ("reserved", "<i4"),
@@ -42,6 +46,13 @@ class CEProblem(ctypes.Structure):
                 ("vocab_start", ctypes.c_int64), ("V_total", ctypes.c_int64),
                 ("ignore_index", ctypes.c_int64), ("label_smoothing", ctypes.c_float),
                 ("reduction", ctypes.c_int32)]
+
+
+class CELinearProblem(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int64), ("D", ctypes.c_int64), ("V", ctypes.c_int64),
+                ("ignore_index", ctypes.c_int64), ("label_smoothing", ctypes.c_float),
+                ("reduction", ctypes.c_int32), ("accum", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class CEError(RuntimeError):
@@ -74,6 +85,11 @@ def lib():
         L.ce_backward.restype = i32
         L.ce_fused_fwd_bwd.argtypes = [prob, P, i32, P, P, P, P, P, P, P, i32, i64, P, sz, P]
         L.ce_fused_fwd_bwd.restype = i32
+        lprob = ctypes.POINTER(CELinearProblem)
+        L.ce_linear_workspace_bytes.argtypes = [lprob, i32]
+        L.ce_linear_workspace_bytes.restype = sz
+        L.ce_linear_fwd_bwd.argtypes = [lprob, P, P, P, P, P, P, P, P, P, P, P, sz, P]
+        L.ce_linear_fwd_bwd.restype = i32
         L.ce_status_str.argtypes = [i32]
         L.ce_status_str.restype = ctypes.c_char_p
         L.ce_version.argtypes = []
@@ -153,6 +169,26 @@ def ce_fused_fwd_bwd(prob, logits, logits_dtype, target, grad_output, loss_rows,
         ctypes.byref(prob), _ptr(logits), int(logits_dtype), _ptr(target), _ptr(grad_output),
         _ptr(loss_rows), _ptr(loss), _ptr(n_valid), _ptr(err_count), _ptr(grad),
         int(grad_dtype), int(ldg), _ptr(ws), int(ws_bytes), _stream(stream)))
+
+
+def make_linear_problem(N, D, V, *, ignore_index=-100, label_smoothing=0.0, reduction="mean",
+                        accum="fp32"):
+    red = REDUCTIONS[reduction] if isinstance(reduction, str) else int(reduction)
+    acc = ACCUMS[accum] if isinstance(accum, str) else int(accum)
+    return CELinearProblem(int(N), int(D), int(V), int(ignore_index), float(label_smoothing),
+                           red, acc, 0)
+
+
+def ce_linear_workspace_bytes(prob, backward):
+    return int(lib().ce_linear_workspace_bytes(ctypes.byref(prob), int(backward)))
+
+
+def ce_linear_fwd_bwd(prob, E, C, target, grad_output, loss_rows, loss, n_valid, err_count, dE,
+                      dC, ws, ws_bytes, stream=None):
+    _check("ce_linear_fwd_bwd", lib().ce_linear_fwd_bwd(
+        ctypes.byref(prob), _ptr(E), _ptr(C), _ptr(target), _ptr(grad_output), _ptr(loss_rows),
+        _ptr(loss), _ptr(n_valid), _ptr(err_count), _ptr(dE), _ptr(dC), _ptr(ws), int(ws_bytes),
+        _stream(stream)))
 
 
 def ce_status_str(status):

@@ -178,3 +178,38 @@ class CrossEntropy(torch.autograd.Function):
 def cross_entropy(logits, target, *, ignore_index=-100, label_smoothing=0.0, reduction="mean"):
     """Differentiable stable cross-entropy over [T, V] logits."""
     return CrossEntropy.apply(logits, target, ignore_index, label_smoothing, reduction)
+
+
+def linear_cross_entropy(E, C, target, *, ignore_index=-100, label_smoothing=0.0,
+                         reduction="mean", grad_output=None, backward=True, accum="fp32",
+                         stream=None):
+    """Cross-entropy of the logits E C^T without forming them (the library's
+    ce_linear_fwd_bwd): E [N, D] and C [V, D] bf16 with contiguous rows.
+    Returns loss, loss_rows, n_valid, err_count and, with ``backward``, the
+    fp32 gradients dE [N, D] and dC [V, D]."""
+    if E.dtype != torch.bfloat16 or C.dtype != torch.bfloat16:
+        raise ValueError("E and C must be bf16")
+    if E.dim() != 2 or C.dim() != 2 or E.shape[1] != C.shape[1]:
+        raise ValueError("E must be [N, D] and C [V, D]")
+    if not (E.is_contiguous() and C.is_contiguous()):
+        raise ValueError("E and C must be contiguous")
+    N, D = E.shape
+    V = C.shape[0]
+    target = _target(target, N)
+    dev = E.device
+    prob = B.make_linear_problem(N, D, V, ignore_index=ignore_index,
+                                 label_smoothing=label_smoothing, reduction=reduction,
+                                 accum=accum)
+    nws = B.ce_linear_workspace_bytes(prob, backward)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    loss_rows = torch.empty(N, dtype=torch.float32, device=dev)
+    n_valid = torch.empty(1, dtype=torch.int32, device=dev)
+    err = torch.empty(1, dtype=torch.int32, device=dev)
+    dE = torch.empty((N, D), dtype=torch.float32, device=dev) if backward else None
+    dC = torch.empty((V, D), dtype=torch.float32, device=dev) if backward else None
+    go = _grad_output(grad_output, reduction, N, dev)
+    B.ce_linear_fwd_bwd(prob, E, C, target, go, loss_rows, loss, n_valid, err, dE, dC, ws, nws,
+                        stream)
+    return {"loss": loss, "loss_rows": loss_rows, "n_valid": n_valid, "err_count": err,
+            "dE": dE, "dC": dC}

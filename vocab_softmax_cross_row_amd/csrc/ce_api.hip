@@ -143,6 +143,72 @@ T *at(void *ws, size_t off) {
 }
 
 
+// ---- linear classifier ------------------------------------------------------
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+int check_linear(const ce_linear_problem *p) {
+    if (!p) return CE_ERR_NULL;
+    if (p->reduction != CE_RED_NONE && p->reduction != CE_RED_SUM &&
+        p->reduction != CE_RED_MEAN)
+        return CE_ERR_REDUCTION;
+    if (!std::isfinite(p->label_smoothing) || p->label_smoothing < 0.0f ||
+        p->label_smoothing >= 1.0f)
+        return CE_ERR_SMOOTHING;
+    if (p->accum != CE_ACC_FP32 && p->accum != CE_ACC_KAHAN) return CE_ERR_ARG;
+    if (p->N < 0 || p->D < 8 || p->D % 8 != 0 || p->V < 1) return CE_ERR_SHAPE;
+    // fragment-major operands: 8 row blocks of 32 rows x (padded K) bf16 must
+    // stay below 2^31 bytes (32-bit buffer offsets); counts are int32
+    const int64_t kmax = ((int64_t)1 << 31) / 512 - 256;
+    if (round_up(p->N, 256) > kmax || round_up(p->V, 256) > kmax ||
+        round_up(p->D, 256) > kmax || p->N > INT32_MAX)
+        return CE_ERR_SHAPE;
+    return CE_OK;
+}
+
+// Padded sizes and workspace layout of ce_linear_fwd_bwd.
+struct LinLayout {
+    int64_t Np;  // tokens padded to 256: rows of Ef and G, K of ETf and GT
+    int64_t Dp;  // hidden size padded to 64: K of Ef and Cf
+    int64_t Dr;  // hidden size padded to 256: rows of ETf and CTf
+    int64_t Vp;  // classes padded to 256: rows of Cf, K of CTf
+    int64_t Vc;  // classes per backward chunk
+    int64_t tiles_v;
+    size_t Ef, Cf, stats, fin, loss_rows, counts, ETf, CTf, rows, G, GT, comp, total;
+};
+
+LinLayout linear_layout(const ce_linear_problem *p, bool backward) {
+    LinLayout l{};
+    const int64_t N = std::max<int64_t>(p->N, 0);
+    l.Np = round_up(std::max<int64_t>(N, 1), 256);
+    l.Dp = round_up(p->D, 64);
+    l.Dr = round_up(p->D, 256);
+    l.Vp = round_up(p->V, 256);
+    l.Vc = std::min<int64_t>(CE_LINEAR_CHUNK, l.Vp);
+    l.tiles_v = l.Vp / 256;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align_up(bytes);
+        return o;
+    };
+    l.Ef = take((size_t)l.Np * l.Dp * 2);
+    l.Cf = take((size_t)l.Vp * l.Dp * 2);
+    l.stats = take((size_t)l.tiles_v * N * sizeof(ce_row_stats));
+    l.fin = take((size_t)N * sizeof(ce_row_final));
+    l.loss_rows = take((size_t)N * sizeof(float));
+    l.counts = take(2 * sizeof(int32_t));
+    if (backward) {
+        l.ETf = take((size_t)l.Dr * l.Np * 2);
+        l.CTf = take((size_t)l.Dr * l.Vp * 2);
+        l.rows = take((size_t)N * kLinRowBytes);
+        l.G = take((size_t)l.Np * l.Vc * 2);
+        l.GT = take((size_t)l.Vc * l.Np * 2);
+        l.comp = take(p->accum == CE_ACC_KAHAN ? (size_t)N * p->D * sizeof(float) : 0);
+    }
+    l.total = off;
+    return l;
+}
+
 #define VCE_TRY(expr)                                                                            \
     do {                                                                                         \
         const hipError_t e_ = (expr);                                                            \
@@ -400,6 +466,146 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
     }
     if (loss && p.reduction != CE_RED_NONE)
         VCE_TRY(launch_reduce(lr, p.T, p.reduction, nv, loss, s));
+    return CE_OK;
+}
+
+size_t ce_linear_workspace_bytes(const ce_linear_problem *prob, int backward) {
+    if (check_linear(prob) != CE_OK) return 0;
+    return linear_layout(prob, backward != 0).total;
+}
+
+int ce_linear_fwd_bwd(const ce_linear_problem *prob, const void *E, const void *C,
+                      const int64_t *target, const float *grad_output, float *loss_rows,
+                      float *loss, int32_t *n_valid, int32_t *err_count, float *dE, float *dC,
+                      void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_linear(prob);
+    if (rc != CE_OK) return rc;
+    const ce_linear_problem &p = *prob;
+    if ((dE == nullptr) != (dC == nullptr)) return CE_ERR_NULL;
+    const bool bwd = dE != nullptr;
+    if (!E || !C || (p.N > 0 && !target)) return CE_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(E) % 16 || reinterpret_cast<uintptr_t>(C) % 16 ||
+        reinterpret_cast<uintptr_t>(dE) % 16 || reinterpret_cast<uintptr_t>(dC) % 16)
+        return CE_ERR_SHAPE;
+    const LinLayout l = linear_layout(prob, bwd);
+    if (!ws || ws_bytes < l.total || reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+        return CE_ERR_WORKSPACE;
+    if (bwd && (overlaps(dE, (size_t)p.N * p.D * 4, E, (size_t)p.N * p.D * 2) ||
+                overlaps(dE, (size_t)p.N * p.D * 4, C, (size_t)p.V * p.D * 2) ||
+                overlaps(dC, (size_t)p.V * p.D * 4, E, (size_t)p.N * p.D * 2) ||
+                overlaps(dC, (size_t)p.V * p.D * 4, C, (size_t)p.V * p.D * 2) ||
+                overlaps(dE, (size_t)p.N * p.D * 4, dC, (size_t)p.V * p.D * 4)))
+        return CE_ERR_ALIAS;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t N = p.N, D = p.D, V = p.V;
+
+    int32_t *nv = n_valid ? n_valid : at<int32_t>(ws, l.counts);
+    VCE_TRY(launch_count(target, N, p.ignore_index, V, nv, err_count, s));
+    float *lr = loss_rows ? loss_rows : at<float>(ws, l.loss_rows);
+    if (N == 0) {
+        if (loss && p.reduction != CE_RED_NONE)
+            VCE_TRY(launch_reduce(nullptr, 0, p.reduction, nv, loss, s));
+        if (bwd)
+            VCE_TRY(launch_zero_f32(dC, V * D, s));
+        return CE_OK;
+    }
+    uint16_t *Ef = at<uint16_t>(ws, l.Ef), *Cf = at<uint16_t>(ws, l.Cf);
+    const uint16_t *Eh = static_cast<const uint16_t *>(E), *Ch = static_cast<const uint16_t *>(C);
+    VCE_TRY(launch_relayout(RelayoutArgs{Eh, N, D, D, Ef, l.Np, l.Dp}, false, s));
+    VCE_TRY(launch_relayout(RelayoutArgs{Ch, V, D, D, Cf, l.Vp, l.Dp}, false, s));
+
+    // forward: per (256-class tile, row) statistics of the logits, merged
+    const bool ls = p.label_smoothing > 0.0f;
+    ce_row_stats *stats = at<ce_row_stats>(ws, l.stats);
+    GemmArgs fg{};
+    fg.A = Ef;
+    fg.B = Cf;
+    fg.a_ks = fg.b_ks = l.Dp;
+    fg.K = l.Dp;
+    fg.M = N;
+    fg.N = V;
+    fg.tiles_m = (int)(l.Np / 256);
+    fg.tiles_n = (int)l.tiles_v;
+    fg.target = target;
+    fg.col_base = 0;
+    fg.stats = stats;
+    VCE_TRY(launch_gemm(fg, GEMM_STATS, ls, s));
+
+    ce_row_final *fin = at<ce_row_final>(ws, l.fin);
+    MergeArgs ma;
+    ma.in = stats;
+    ma.S = (int)l.tiles_v;
+    ma.T = N;
+    ma.target = target;
+    ma.ignore_index = p.ignore_index;
+    ma.V_total = V;
+    ma.eps = p.label_smoothing;
+    ma.stats_out = nullptr;
+    ma.fin = fin;
+    ma.loss_rows = lr;
+    VCE_TRY(launch_merge(ma, s));
+    if (loss && p.reduction != CE_RED_NONE)
+        VCE_TRY(launch_reduce(lr, N, p.reduction, nv, loss, s));
+    if (!bwd) return CE_OK;
+
+    // backward: per class chunk, G and G^T (bf16), then dC rows and dE
+    uint16_t *ETf = at<uint16_t>(ws, l.ETf), *CTf = at<uint16_t>(ws, l.CTf);
+    VCE_TRY(launch_relayout(RelayoutArgs{Eh, N, D, D, ETf, l.Dr, l.Np}, true, s));
+    VCE_TRY(launch_relayout(RelayoutArgs{Ch, V, D, D, CTf, l.Dr, l.Vp}, true, s));
+    void *rows = at<char>(ws, l.rows);
+    LinRowArgs ra{fin, target, nv, grad_output, p.reduction, p.label_smoothing, N, V, rows};
+    VCE_TRY(launch_linear_rowconst(ra, s));
+    void *G = at<char>(ws, l.G), *GT = at<char>(ws, l.GT);
+    float *comp = p.accum == CE_ACC_KAHAN ? at<float>(ws, l.comp) : nullptr;
+    for (int64_t c0 = 0; c0 < V; c0 += l.Vc) {
+        const int64_t w = std::min(l.Vc, V - c0), wp = round_up(w, 256);
+        GemmArgs gg{};
+        gg.A = Ef;
+        gg.B = reinterpret_cast<const char *>(Cf) + (c0 / 32) * (l.Dp / 16) * 1024;
+        gg.a_ks = gg.b_ks = l.Dp;
+        gg.K = l.Dp;
+        gg.M = N;
+        gg.N = w;
+        gg.tiles_m = (int)(l.Np / 256);
+        gg.tiles_n = (int)(wp / 256);
+        gg.col_base = c0;
+        gg.rows = rows;
+        gg.G = G;
+        gg.ldg = wp;
+        gg.GT = GT;
+        gg.ldgt = l.Np;
+        VCE_TRY(launch_gemm(gg, GEMM_GRAD, ls, s));
+
+        GemmArgs cg{}; // dC[c0 .. c0 + w) = G^T E
+        cg.A = GT;
+        cg.B = ETf;
+        cg.a_ks = cg.b_ks = l.Np;
+        cg.K = l.Np;
+        cg.M = w;
+        cg.N = D;
+        cg.tiles_m = (int)(wp / 256);
+        cg.tiles_n = (int)(l.Dr / 256);
+        cg.out = dC + c0 * D;
+        cg.ldo = D;
+        VCE_TRY(launch_gemm(cg, GEMM_STORE, false, s));
+
+        GemmArgs eg{}; // dE += G C[c0 .. c0 + w)
+        eg.A = G;
+        eg.B = CTf;
+        eg.a_ks = wp;
+        eg.b_ks = l.Vp;
+        eg.b_kb0 = (int)(c0 / 16);
+        eg.K = wp;
+        eg.M = N;
+        eg.N = D;
+        eg.tiles_m = (int)(l.Np / 256);
+        eg.tiles_n = (int)(l.Dr / 256);
+        eg.out = dE;
+        eg.ldo = D;
+        eg.comp = comp;
+        eg.first = c0 == 0;
+        VCE_TRY(launch_gemm(eg, comp ? GEMM_KAHAN : GEMM_ADD, false, s));
+    }
     return CE_OK;
 }
 

@@ -70,6 +70,61 @@ struct GradArgs {
     int64_t chunk_cols;
 };
 
+// ---- linear classifier (ce_linear.hip) ------------------------------------
+constexpr int kLinRowBytes = 48;         // per-row gradient constants
+constexpr int kGemmLdsBytes = 147456;    // 144 KB of the CU's 160 KB
+enum { GEMM_STATS = 0, GEMM_GRAD = 1, GEMM_STORE = 2, GEMM_ADD = 3, GEMM_KAHAN = 4 };
+
+// X [R, K] row-major bf16 (stride ld) -> fragment-major Y padded to [Rp, Kp]
+// (of X, or of X^T when transposed: then Y's rows are X's columns)
+struct RelayoutArgs {
+    const uint16_t *X;
+    int64_t R, K, ld;
+    uint16_t *Y;
+    int64_t Rp, Kp;
+};
+
+struct LinRowArgs {
+    const ce_row_final *fin;
+    const int64_t *target;
+    const int32_t *n_valid;
+    const float *grad_output;
+    int reduction;
+    float eps;
+    int64_t N, V;
+    void *rows; // [N] x kLinRowBytes
+};
+
+// out[M, N] = A[M, K] B[N, K]^T, A and B fragment-major bf16
+struct GemmArgs {
+    const void *A, *B;
+    int64_t a_ks, b_ks; // stored (padded) K of A and B: the row pitch of the blocks
+    int a_kb0, b_kb0;   // first 16-column K block this product reads
+    int64_t K;          // K of the product (multiple of 64)
+    int64_t M, N;       // valid output rows and columns
+    int tiles_m, tiles_n;
+    // GEMM_STATS
+    const int64_t *target;
+    int64_t col_base;   // class of output column 0
+    ce_row_stats *stats; // [tiles_n][M]
+    // GEMM_GRAD
+    const void *rows;   // per-row constants [M]
+    void *G;            // fragment-major, rows = tokens, K = classes (ldg)
+    int64_t ldg;
+    void *GT;           // fragment-major, rows = classes, K = tokens (ldgt)
+    int64_t ldgt;
+    // GEMM_STORE / ADD / KAHAN
+    float *out;
+    int64_t ldo;
+    float *comp;
+    int first;
+};
+
+hipError_t launch_relayout(const RelayoutArgs &a, bool transpose, hipStream_t stream);
+hipError_t launch_linear_rowconst(const LinRowArgs &a, hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs &g, int epi, bool ls, hipStream_t stream);
+hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t stream);
+
 hipError_t launch_count(const int64_t *target, int64_t T, int64_t ignore_index, int64_t V_total,
                         int32_t *n_valid, int32_t *err_count, hipStream_t stream);
 hipError_t launch_reduce(const float *loss_rows, int64_t T, int reduction, const int32_t *n_valid,

@@ -1,0 +1,526 @@
+// Cross-entropy of a linear classifier: the logits Z = E C^T are formed tile
+// by tile on the matrix cores and never stored (apple/ml-cross-entropy issue
+// #14, linear_cross_entropy(embeddings, classifier, labels)).
+//
+// Every product here is out[M, N] = A[M, K] B[N, K]^T with bf16 operands and
+// fp32 accumulation on v_mfma_f32_32x32x16_bf16.  Operands are kept in a
+// "fragment-major" layout: the matrix is cut into blocks of 32 rows x 16
+// K-columns (1 KB), block (rb, kb) at byte (rb * Ks/16 + kb) * 1024 where Ks
+// is the stored (padded) K, and inside a block lane L's 16 bytes at L * 16
+// hold row rb*32 + L%32, K-columns kb*16 + 8*(L/32) .. +7 -- exactly the
+// A or B register fragment of that MFMA.  A wave fills one LDS block with
+// one 16-byte-per-lane buffer->LDS load of 1 KB of contiguous memory, and
+// reads one fragment with one conflict-free ds_read_b128.  Padding (rows to
+// a multiple of 256, K to a multiple of 64) is zero, so loads need no
+// bounds checks.
+//
+// Accumulator layout of v_mfma_f32_32x32x16_bf16 (32 x 32 fp32, 16 values
+// per lane): register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
+// column l%32.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ce_device.h"
+#include "ce_launch.h"
+
+namespace vce {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+constexpr int kGT = 256;                 // 4 waves, 2 x 2 over the tile
+constexpr int kTile = 256;               // output tile 256 x 256
+constexpr int kBK = 64;                  // K per LDS stage
+constexpr int kStage = 2 * 8 * 4 * 1024; // A and B: 8 row blocks x 4 K blocks each
+constexpr int kSuperM = 4, kSuperN = 8;  // 32 tiles one XCD works on together
+
+struct LinRow {
+    GradConst c;
+    int32_t t;     // target class
+    int32_t valid; // 1 if the row has a gradient
+};
+static_assert(sizeof(LinRow) == kLinRowBytes, "row constant size");
+static_assert(kGemmLdsBytes >= 2 * kStage + kTile * (int)sizeof(LinRow), "LDS budget");
+
+__device__ __forceinline__ int64_t frag_off(int64_t rb, int64_t kb, int64_t Ks) {
+    return (rb * (Ks / 16) + kb) * 1024;
+}
+
+// ---------------------------------------------------------------------------
+// Re-layout of a row-major bf16 matrix X [R, K] (leading dimension ld, K a
+// multiple of 8) into fragment-major form, padded to [Rp, Kp] with zeros.
+// One thread writes one 16-byte fragment slot.
+// ---------------------------------------------------------------------------
+constexpr int kRelayoutThreads = 256;
+
+__global__ __launch_bounds__(kRelayoutThreads) void k_relayout(RelayoutArgs a) {
+    const int64_t s = (int64_t)blockIdx.x * kRelayoutThreads + threadIdx.x;
+    if (s >= a.Rp * a.Kp / 8) return;
+    const int64_t blk = s / 64;
+    const int L = (int)(s % 64);
+    const int64_t rb = blk / (a.Kp / 16), kb = blk % (a.Kp / 16);
+    const int64_t r = rb * 32 + (L & 31);
+    const int64_t k = kb * 16 + 8 * (L >> 5);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (r < a.R && k < a.K) v = *reinterpret_cast<const u32x4 *>(a.X + r * a.ld + k);
+    *reinterpret_cast<u32x4 *>(a.Y + s * 8) = v;
+}
+
+// Transposed re-layout: Y = fragment-major form of X^T, padded to [Rp, Kp]
+// (Y's rows are X's columns, Y's K is X's rows).  A workgroup moves a
+// 64 x 64 tile through LDS: 16-byte row loads of X, 16-byte slot stores of Y.
+__global__ __launch_bounds__(kRelayoutThreads) void k_relayout_t(RelayoutArgs a) {
+    __shared__ uint16_t t[64][64 + 2];
+    const int tid = threadIdx.x;
+    const int64_t tiles_y = a.Rp / 64;                        // tiles along Y rows
+    const int64_t x0 = (int64_t)(blockIdx.x / tiles_y) * 64; // X rows = Y K-columns
+    const int64_t y0 = (int64_t)(blockIdx.x % tiles_y) * 64; // X cols = Y rows
+    if (x0 >= a.Kp) return;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int slot = tid + q * kRelayoutThreads;
+        const int lr = slot / 8, lc = (slot % 8) * 8;
+        const int64_t r = x0 + lr, c = y0 + lc;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r < a.R && c < a.K) v = *reinterpret_cast<const u32x4 *>(a.X + r * a.ld + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            t[lr][lc + 2 * e] = (uint16_t)(v[e] & 0xffffu);
+            t[lr][lc + 2 * e + 1] = (uint16_t)(v[e] >> 16);
+        }
+    }
+    __syncthreads();
+    // 2 row blocks x 4 K blocks of Y = 512 slots, 2 per thread
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int slot = tid + q * kRelayoutThreads;
+        const int b = slot / 64, L = slot % 64;
+        const int brow = b / 4, bk = b % 4;
+        const int yr = brow * 32 + (L & 31);   // Y row in the tile  (X column)
+        const int yk = bk * 16 + 8 * (L >> 5); // Y K in the tile    (X row)
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            v[e] = (uint32_t)t[yk + 2 * e][yr] | ((uint32_t)t[yk + 2 * e + 1][yr] << 16);
+        const int64_t off = frag_off((y0 >> 5) + brow, (x0 >> 4) + bk, a.Kp);
+        *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(a.Y) + off + L * 16) = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Per-row gradient constants after the merge.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_linear_rowconst(LinRowArgs a) {
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (r >= a.N) return;
+    const ce_row_final f = a.fin[r];
+    LinRow o;
+    o.t = (int32_t)a.target[r];
+    o.valid = (f.status == 1) ? 1 : 0;
+    o.c = GradConst{};
+    if (o.valid) {
+        const double k = row_scale(a.reduction, a.grad_output, a.n_valid, r);
+        o.c = grad_constants(f.lse, f.gt, k, (double)a.eps, (double)a.V);
+    }
+    reinterpret_cast<LinRow *>(a.rows)[r] = o;
+}
+
+// ---------------------------------------------------------------------------
+// The GEMM, with its epilogues.
+// ---------------------------------------------------------------------------
+
+// Tile of workgroup b.  Workgroups go round-robin over the 8 XCDs; the 32
+// consecutive workgroups of one XCD get one 4 x 8 super-tile, so they share
+// its A and B blocks in that XCD's L2.  False for the padding workgroups.
+__device__ __forceinline__ bool tile_of(int64_t b, int tiles_m, int tiles_n, int &tm, int &tn) {
+    const int64_t x = b % kXcds, j = b / kXcds;
+    const int64_t s = (j / (kSuperM * kSuperN)) * kXcds + x;
+    const int pos = (int)(j % (kSuperM * kSuperN));
+    const int64_t sn_count = (tiles_n + kSuperN - 1) / kSuperN;
+    const int64_t sm = s / sn_count, sn = s % sn_count;
+    tm = (int)(sm * kSuperM + pos / kSuperN);
+    tn = (int)(sn * kSuperN + pos % kSuperN);
+    return tm < tiles_m && tn < tiles_n;
+}
+
+template <int EPI, bool LS>
+__global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm(GemmArgs g) {
+    extern __shared__ __attribute__((aligned(16))) u32x4 lds[];
+    char *lbase = reinterpret_cast<char *>(lds);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    int tm, tn;
+    if (!tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn)) return;
+    const int64_t row0 = (int64_t)tm * kTile, col0 = (int64_t)tn * kTile;
+
+    // the 8 row blocks of A and of B this tile reads, as buffer resources
+    const int64_t a_span = (int64_t)8 * 32 * g.a_ks * 2, b_span = (int64_t)8 * 32 * g.b_ks * 2;
+    const char *abase = reinterpret_cast<const char *>(g.A) + (int64_t)tm * a_span;
+    const char *bbase = reinterpret_cast<const char *>(g.B) + (int64_t)tn * b_span;
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void *)abase, 0, (int)a_span, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void *)bbase, 0, (int)b_span, 0x00020000);
+    const int nk = (int)(g.K / kBK);
+    const int a_kbs = (int)(g.a_ks / 16), b_kbs = (int)(g.b_ks / 16);
+
+    // wave w loads row blocks 2w and 2w+1 (4 K blocks each) of A and of B
+    auto load_stage = [&](int kt, int buf) {
+        char *st = lbase + buf * kStage;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int rbl = 2 * wave + (q >> 2), kbl = q & 3;
+            const int kb = g.a_kb0 + kt * 4 + kbl;
+            const int loff = (rbl * 4 + kbl) * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(st + loff), 16, lane * 16,
+                                                     (rbl * a_kbs + kb) * 1024, 0, 0);
+            const int kbb = g.b_kb0 + kt * 4 + kbl;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(st + 32768 + loff), 16,
+                                                     lane * 16, (rbl * b_kbs + kbb) * 1024, 0, 0);
+        }
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    load_stage(0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        __builtin_amdgcn_s_waitcnt(0x0070); // vmcnt(0) lgkmcnt(0): this stage has landed
+        __syncthreads();                     // ... for every wave; the other buffer is free
+        if (kt + 1 < nk) load_stage(kt + 1, (kt + 1) & 1);
+        const char *st = lbase + (kt & 1) * kStage;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            bf16x8 fa[4], fb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                fa[i] = *reinterpret_cast<const bf16x8 *>(st + ((wm * 4 + i) * 4 + kb) * 1024 +
+                                                          lane * 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                fb[j] = *reinterpret_cast<const bf16x8 *>(
+                    st + 32768 + ((wn * 4 + j) * 4 + kb) * 1024 + lane * 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j],
+                                                                         0, 0, 0);
+        }
+    }
+    __syncthreads(); // every wave is done with the operand stages
+
+    // Epilogues work on one row block i (32 rows x 128 columns per wave) at a
+    // time, staged through the wave's own LDS slab so that the row-wise work
+    // and the global accesses are contiguous: lanes 16q..16q+15 then own row
+    // 4*it + q of the block and 8 consecutive columns each.
+    const int h = lane >> 5, lc = lane & 31;
+    constexpr int kPitch = 132; // floats per slab row (keeps 16-byte reads spread over banks)
+    float *slab = reinterpret_cast<float *>(lbase) + wave * 32 * kPitch;
+    const int sub = lane >> 4, c8 = (lane & 15) * 8; // row-pass lane role
+    auto stage = [&](int i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                slab[(8 * (r >> 2) + 4 * h + (r & 3)) * kPitch + j * 32 + lc] = acc[i][j][r];
+    };
+
+    if constexpr (EPI == GEMM_STATS) {
+        // per row of the tile: max and sum of exp over this tile's columns
+        // with the target left out, the target logit, the sum of all logits
+        char *ex = lbase + 4 * 32 * kPitch * 4;                  // after the slabs
+        int32_t *t_l = reinterpret_cast<int32_t *>(ex);           // [256] target column or -1
+        float *pm = reinterpret_cast<float *>(ex + 1024);         // [2][256] per column half
+        float *ps = reinterpret_cast<float *>(ex + 3072);
+        float *pz = reinterpret_cast<float *>(ex + 5120);
+        float *zt = reinterpret_cast<float *>(ex + 7168);         // [256]
+        int32_t *own = reinterpret_cast<int32_t *>(ex + 8192);    // [256]
+        {
+            const int64_t r = row0 + tid;
+            int32_t tl = -1;
+            if (r < g.M) {
+                const int64_t t = g.target[r] - g.col_base - col0;
+                if (t >= 0 && t < kTile && col0 + t < g.N) tl = (int32_t)t;
+            }
+            t_l[tid] = tl;
+            zt[tid] = 0.0f;
+            own[tid] = 0;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            __syncthreads();
+            stage(i);
+            __syncthreads();
+#pragma unroll 2
+            for (int it = 0; it < 8; ++it) {
+                const int rl = 4 * it + sub;                      // row in the block
+                const int row = wm * 128 + i * 32 + rl;           // row in the tile
+                const int cb = wn * 128 + c8;                     // first column in the tile
+                const float *src = slab + rl * kPitch + c8;
+                const u32x4 p0 = *reinterpret_cast<const u32x4 *>(src);
+                const u32x4 p1 = *reinterpret_cast<const u32x4 *>(src + 4);
+                float z[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    z[e] = __uint_as_float(p0[e]);
+                    z[4 + e] = __uint_as_float(p1[e]);
+                }
+                const int tl = t_l[row];
+                float mx = ninf(), sz = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const bool in = col0 + cb + e < g.N;
+                    if (LS && in) sz += z[e];
+                    if (cb + e == tl) {
+                        zt[row] = z[e];
+                        own[row] = 1;
+                    }
+                    if (!in || cb + e == tl) z[e] = ninf();
+                    mx = fmaxf(mx, z[e]);
+                }
+#pragma unroll
+                for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+                float s = 0.0f;
+                if (mx != ninf()) {
+                    const float K = mx * kL2E;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) s += fast_exp2(fmaf(z[e], kL2E, -K));
+                }
+#pragma unroll
+                for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+                if (LS) {
+#pragma unroll
+                    for (int o = 8; o > 0; o >>= 1) sz += __shfl_xor(sz, o, 64);
+                }
+                if ((lane & 15) == 0) {
+                    pm[wn * 256 + row] = mx;
+                    ps[wn * 256 + row] = s;
+                    pz[wn * 256 + row] = sz;
+                }
+            }
+        }
+        __syncthreads();
+        const int64_t r = row0 + tid;
+        if (r < g.M) {
+            const float m0 = pm[tid], m1 = pm[256 + tid];
+            const float M = fmaxf(m0, m1);
+            double s = 0.0;
+            if (m0 != ninf()) s += (double)ps[tid] * exp((double)m0 - (double)M);
+            if (m1 != ninf()) s += (double)ps[256 + tid] * exp((double)m1 - (double)M);
+            ce_row_stats o;
+            o.m = M;
+            o.zt = zt[tid];
+            o.own = own[tid];
+            o.reserved = 0;
+            o.s = s;
+            o.sz = LS ? (double)pz[tid] + (double)pz[256 + tid] : 0.0;
+            g.stats[(int64_t)tn * g.M + r] = o;
+        }
+    } else if constexpr (EPI == GEMM_GRAD) {
+        // G = k (softmax - q) of the tile, rounded to bf16 (RNE), written in
+        // fragment-major form twice: G (rows = tokens, K = classes) from the
+        // row pass, where a lane holds 8 consecutive classes of one token,
+        // and GT (rows = classes, K = tokens) from a column pass over the
+        // bf16 copy of the block, where a lane gathers 8 consecutive tokens
+        // of one class.
+        constexpr int kBPitch = 136; // bf16 per row of the bf16 slab
+        uint16_t *bslab = reinterpret_cast<uint16_t *>(lbase + 4 * 32 * kPitch * 4) +
+                          wave * 32 * kBPitch;
+        LinRow *rc = reinterpret_cast<LinRow *>(lbase + 4 * 32 * kPitch * 4 +
+                                                4 * 32 * kBPitch * 2);
+        {
+            // rows past M get all-zero constants: valid = 0
+            const int64_t r = row0 + tid;
+            u32x4 v[3] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+            if (r < g.M) {
+                const u32x4 *src = reinterpret_cast<const u32x4 *>(g.rows) + r * 3;
+#pragma unroll
+                for (int q = 0; q < 3; ++q) v[q] = src[q];
+            }
+            u32x4 *dst = reinterpret_cast<u32x4 *>(rc + tid);
+#pragma unroll
+            for (int q = 0; q < 3; ++q) dst[q] = v[q];
+        }
+        char *GT = reinterpret_cast<char *>(g.GT);
+        char *G = reinterpret_cast<char *>(g.G);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            __syncthreads();
+            stage(i);
+            __syncthreads();
+#pragma unroll 2
+            for (int it = 0; it < 8; ++it) {
+                const int rl = 4 * it + sub;
+                const int64_t n = row0 + wm * 128 + i * 32 + rl;
+                const int64_t v0 = col0 + wn * 128 + c8;
+                const float *src = slab + rl * kPitch + c8;
+                const u32x4 p0 = *reinterpret_cast<const u32x4 *>(src);
+                const u32x4 p1 = *reinterpret_cast<const u32x4 *>(src + 4);
+                const LinRow R = rc[wm * 128 + i * 32 + rl];
+                const int64_t tcl = (int64_t)R.t - g.col_base;
+                float gv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float z = __uint_as_float(e < 4 ? p0[e] : p1[e - 4]);
+                    const int64_t v = v0 + e;
+                    float x = 0.0f;
+                    if (R.valid && v < g.N)
+                        x = (v == tcl) ? R.c.gk : grad_elem<CE_BF16, LS>(z, R.c);
+                    gv[e] = x;
+                }
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(gv[2 * e], gv[2 * e + 1]);
+                *reinterpret_cast<u32x4 *>(bslab + rl * kBPitch + c8) = w;
+                const int64_t off = frag_off(n >> 5, v0 >> 4, g.ldg) +
+                                    (int64_t)((n & 31) + 32 * ((v0 & 15) >> 3)) * 16;
+                *reinterpret_cast<u32x4 *>(G + off) = w;
+            }
+            __syncthreads();
+            // column pass: fragment f*64 + lane = (class c, tokens 8 tau .. +7)
+#pragma unroll 2
+            for (int f = 0; f < 8; ++f) {
+                const int phi = f * 64 + lane;
+                const int c = phi & 127, tau = phi >> 7;
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = (uint32_t)bslab[(8 * tau + 2 * e) * kBPitch + c] |
+                           ((uint32_t)bslab[(8 * tau + 2 * e + 1) * kBPitch + c] << 16);
+                const int64_t v = col0 + wn * 128 + c;
+                const int64_t n0 = row0 + wm * 128 + i * 32 + 8 * tau;
+                const int64_t off = frag_off(v >> 5, n0 >> 4, g.ldgt) +
+                                    (int64_t)((v & 31) + 32 * ((n0 & 15) >> 3)) * 16;
+                *reinterpret_cast<u32x4 *>(GT + off) = w;
+            }
+        }
+    } else {
+        // plain fp32 result: store, add, or add with Kahan compensation;
+        // lanes write 16 bytes, a row's 128 columns are 512 contiguous bytes
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            __syncthreads();
+            stage(i);
+            __syncthreads();
+#pragma unroll 2
+            for (int it = 0; it < 8; ++it) {
+                const int rl = 4 * it + sub;
+                const int64_t row = row0 + wm * 128 + i * 32 + rl;
+                const int64_t col = col0 + wn * 128 + c8;
+                if (row >= g.M || col >= g.N) continue;
+                const float *src = slab + rl * kPitch + c8;
+#pragma unroll
+                for (int hh = 0; hh < 2; ++hh) {
+                    u32x4 a = *reinterpret_cast<const u32x4 *>(src + 4 * hh);
+                    u32x4 *o = reinterpret_cast<u32x4 *>(g.out + row * g.ldo + col + 4 * hh);
+                    if constexpr (EPI == GEMM_STORE) {
+                        *o = a;
+                    } else if constexpr (EPI == GEMM_ADD) {
+                        if (!g.first) {
+                            const u32x4 b = *o;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                a[e] = __float_as_uint(__uint_as_float(a[e]) + __uint_as_float(b[e]));
+                        }
+                        *o = a;
+                    } else {
+                        u32x4 *cp = reinterpret_cast<u32x4 *>(g.comp + row * g.ldo + col + 4 * hh);
+                        if (g.first) {
+                            *o = a;
+                            *cp = u32x4{0u, 0u, 0u, 0u};
+                        } else {
+                            // Kahan: c carries what earlier additions lost
+                            const u32x4 sv = *o, cv = *cp;
+                            u32x4 so, co;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float sum = __uint_as_float(sv[e]);
+                                const float y = __uint_as_float(a[e]) - __uint_as_float(cv[e]);
+                                const float t = sum + y;
+                                co[e] = __float_as_uint((t - sum) - y);
+                                so[e] = __float_as_uint(t);
+                            }
+                            *o = so;
+                            *cp = co;
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+// zero-fill (a kernel rather than a memset node, so callers may capture it)
+__global__ __launch_bounds__(256) void k_zero_f32(float *p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_relayout(const RelayoutArgs &a, bool transpose, hipStream_t stream) {
+    if (!transpose) {
+        const int64_t slots = a.Rp * a.Kp / 8;
+        const dim3 grid((unsigned)((slots + kRelayoutThreads - 1) / kRelayoutThreads));
+        hipLaunchKernelGGL(k_relayout, grid, dim3(kRelayoutThreads), 0, stream, a);
+    } else {
+        const dim3 grid((unsigned)((a.Rp / 64) * (a.Kp / 64)));
+        hipLaunchKernelGGL(k_relayout_t, grid, dim3(kRelayoutThreads), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_linear_rowconst(const LinRowArgs &a, hipStream_t stream) {
+    const dim3 grid((unsigned)((a.N + 255) / 256));
+    hipLaunchKernelGGL(k_linear_rowconst, grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int EPI, bool LS>
+static hipError_t gemm_launch(const GemmArgs &g, hipStream_t stream) {
+    static bool attr = false;
+    if (!attr) {
+        hipError_t e = hipFuncSetAttribute((const void *)k_gemm<EPI, LS>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           kGemmLdsBytes);
+        if (e != hipSuccess) return e;
+        attr = true;
+    }
+    const int64_t supers = ((g.tiles_m + kSuperM - 1) / kSuperM) *
+                           ((g.tiles_n + kSuperN - 1) / kSuperN);
+    const int64_t groups = (supers + kXcds - 1) / kXcds;
+    const dim3 grid((unsigned)(groups * kXcds * kSuperM * kSuperN));
+    hipLaunchKernelGGL((k_gemm<EPI, LS>), grid, dim3(kGT), kGemmLdsBytes, stream, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs &g, int epi, bool ls, hipStream_t stream) {
+    switch (epi) {
+    case GEMM_STATS: return ls ? gemm_launch<GEMM_STATS, true>(g, stream)
+                               : gemm_launch<GEMM_STATS, false>(g, stream);
+    case GEMM_GRAD: return ls ? gemm_launch<GEMM_GRAD, true>(g, stream)
+                              : gemm_launch<GEMM_GRAD, false>(g, stream);
+    case GEMM_STORE: return gemm_launch<GEMM_STORE, false>(g, stream);
+    case GEMM_ADD: return gemm_launch<GEMM_ADD, false>(g, stream);
+    case GEMM_KAHAN: return gemm_launch<GEMM_KAHAN, false>(g, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+} // namespace vce
