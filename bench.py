@@ -23,6 +23,11 @@ Extra objects in the line:
   split_v       the vocabulary split in two 64128-column shards with label
                 smoothing 0.1: ce_forward per shard, ce_merge_shard_stats,
                 ce_backward per shard, timed the same way.
+  linear_ce     cross-entropy of a linear classifier without stored logits
+                (ce_linear_fwd_bwd): E [8192, 2048] and C [128256, 2048] bf16,
+                loss + dE + dC; MFMA roofline: 4 products of 2 N V D flops
+                (forward logits, recomputed logits, dE, dC) against the
+                2.5 PFLOP/s dense bf16 peak.
 """
 import argparse
 import hashlib
@@ -112,6 +117,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-split", action="store_true", help="skip the split-V measurement")
+    ap.add_argument("--no-linear", action="store_true", help="skip the linear-classifier run")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain copy of known size (for counter scaling)")
     args = ap.parse_args()
@@ -207,6 +213,41 @@ def main():
                  "algorithmic_bytes": sb, "frac_of_peak": round(sb / (sms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         print(f"# split-V: {sms:.4f} ms/step", file=sys.stderr, flush=True)
 
+    linear = None
+    if not args.no_linear:
+        lc = S.LINEAR
+        E, Cw, tl = S.generate_linear(lc, device=dev)
+        lp = B.make_linear_problem(lc.N, lc.D, lc.V, ignore_index=lc.ignore_index)
+        nlw = B.ce_linear_workspace_bytes(lp, 1)
+        lws = torch.empty(nlw, dtype=torch.uint8, device=dev)
+        lrows = torch.empty(lc.N, dtype=torch.float32, device=dev)
+        dE = torch.empty((lc.N, lc.D), dtype=torch.float32, device=dev)
+        dC = torch.empty((lc.V, lc.D), dtype=torch.float32, device=dev)
+
+        def linear_step():
+            B.ce_linear_fwd_bwd(lp, E, Cw, tl, None, lrows, loss, n_valid, err, dE, dC, lws,
+                                nlw, stream)
+
+        klin = max(1, args.steps // 10)
+        for _ in range(2):
+            linear_step()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(klin):
+            linear_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        lms = e0.elapsed_time(e1) / klin
+        flops = 4 * 2 * lc.N * lc.V * lc.D
+        tfs = flops / (lms * 1e-3) / 1e12
+        linear = {"workload": f"E [{lc.N}, {lc.D}] x C [{lc.V}, {lc.D}] bf16, loss + dE + dC "
+                              "(fp32), logits never stored",
+                  "steps": klin, "ms_per_step": round(lms, 3), "TFLOP/s": round(tfs, 1),
+                  "algorithmic_flops": flops, "peak_TFLOP/s": 2500.0,
+                  "frac_of_peak": round(tfs / 2500.0, 4), "loss": round(loss.item(), 6)}
+        print(f"# linear CE: {lms:.3f} ms/step, {tfs:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del E, Cw, lws, dE, dC
+
     if args.copy_calibration:
         # a plain device copy of known size for scaling the HBM counters
         src = logits.view(torch.uint8).reshape(-1)[: 1 << 31]
@@ -242,6 +283,7 @@ def main():
                      "traffic": counter_traffic(), "algorithmic_bytes": nbytes},
         "cpu_baseline": cpu,
         "split_v": split,
+        "linear_ce": linear,
     }
     print(json.dumps(out), flush=True)
 

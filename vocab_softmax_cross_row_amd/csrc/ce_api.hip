@@ -532,18 +532,9 @@ int ce_linear_fwd_bwd(const ce_linear_problem *prob, const void *E, const void *
     VCE_TRY(launch_gemm(fg, GEMM_STATS, ls, s));
 
     ce_row_final *fin = at<ce_row_final>(ws, l.fin);
-    MergeArgs ma;
-    ma.in = stats;
-    ma.S = (int)l.tiles_v;
-    ma.T = N;
-    ma.target = target;
-    ma.ignore_index = p.ignore_index;
-    ma.V_total = V;
-    ma.eps = p.label_smoothing;
-    ma.stats_out = nullptr;
-    ma.fin = fin;
-    ma.loss_rows = lr;
-    VCE_TRY(launch_merge(ma, s));
+    LinMergeArgs ma{stats, (int)l.tiles_v, N, V, target, p.ignore_index, p.label_smoothing,
+                    fin, lr};
+    VCE_TRY(launch_linear_merge(ma, s));
     if (loss && p.reduction != CE_RED_NONE)
         VCE_TRY(launch_reduce(lr, N, p.reduction, nv, loss, s));
     if (!bwd) return CE_OK;

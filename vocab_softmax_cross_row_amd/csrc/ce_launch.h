@@ -106,7 +106,7 @@ struct GemmArgs {
     // GEMM_STATS
     const int64_t *target;
     int64_t col_base;   // class of output column 0
-    ce_row_stats *stats; // [tiles_n][M]
+    ce_row_stats *stats; // [M][tiles_n]
     // GEMM_GRAD
     const void *rows;   // per-row constants [M]
     void *G;            // fragment-major, rows = tokens, K = classes (ldg)
@@ -120,6 +120,18 @@ struct GemmArgs {
     int first;
 };
 
+struct LinMergeArgs {
+    const ce_row_stats *stats; // [N][S]
+    int S;
+    int64_t N, V;
+    const int64_t *target;
+    int64_t ignore_index;
+    float eps;
+    ce_row_final *fin;
+    float *loss_rows;
+};
+
+hipError_t launch_linear_merge(const LinMergeArgs &a, hipStream_t stream);
 hipError_t launch_relayout(const RelayoutArgs &a, bool transpose, hipStream_t stream);
 hipError_t launch_linear_rowconst(const LinRowArgs &a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs &g, int epi, bool ls, hipStream_t stream);

@@ -197,23 +197,33 @@ void k_gemm(GemmArgs g) {
         __syncthreads();                     // ... for every wave; the other buffer is free
         if (kt + 1 < nk) load_stage(kt + 1, (kt + 1) & 1);
         const char *st = lbase + (kt & 1) * kStage;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            bf16x8 fa[4], fb[4];
+        // fragments of K block kb+1 are read while the 16 MFMAs of kb run,
+        // so the LDS latency hides behind matrix work (the scheduling
+        // barriers keep the compiler from sinking the reads to their uses)
+        bf16x8 fa[2][4], fb[2][4];
+        auto read_frags = [&](int kb, int set) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                fa[i] = *reinterpret_cast<const bf16x8 *>(st + ((wm * 4 + i) * 4 + kb) * 1024 +
-                                                          lane * 16);
+                fa[set][i] = *reinterpret_cast<const bf16x8 *>(
+                    st + ((wm * 4 + i) * 4 + kb) * 1024 + lane * 16);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                fb[j] = *reinterpret_cast<const bf16x8 *>(
+                fb[set][j] = *reinterpret_cast<const bf16x8 *>(
                     st + 32768 + ((wn * 4 + j) * 4 + kb) * 1024 + lane * 16);
+        };
+        read_frags(0, 0);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int cur = kb & 1;
+            if (kb + 1 < 4) read_frags(kb + 1, cur ^ 1);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j],
-                                                                         0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j],
+                                                                         acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
     __syncthreads(); // every wave is done with the operand stages
@@ -323,7 +333,7 @@ void k_gemm(GemmArgs g) {
             o.reserved = 0;
             o.s = s;
             o.sz = LS ? (double)pz[tid] + (double)pz[256 + tid] : 0.0;
-            g.stats[(int64_t)tn * g.M + r] = o;
+            g.stats[r * g.tiles_n + tn] = o;
         }
     } else if constexpr (EPI == GEMM_GRAD) {
         // G = k (softmax - q) of the tile, rounded to bf16 (RNE), written in
@@ -459,6 +469,65 @@ void k_gemm(GemmArgs g) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Merge of the per-tile statistics of each row ([M][S], row-major) and the
+// finalize: one wave per row, shards spread over the lanes, combined by a
+// fixed butterfly (deterministic).  Same merge and finalize as the shard
+// merge: M = max m_k, s = sum s_k exp(m_k - M), zt, own and sz summed.
+// ---------------------------------------------------------------------------
+constexpr int kMergeWaves = 4;
+
+__global__ __launch_bounds__(kMergeWaves * kWave) void k_linear_merge(LinMergeArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t r = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
+    if (r >= a.N) return;
+    const ce_row_stats *in = a.stats + r * a.S;
+    float m = ninf();
+    for (int k = lane; k < a.S; k += kWave) m = fmaxf(m, in[k].m);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
+    const double M = (double)m;
+    double s = 0.0, zt = 0.0, sz = 0.0;
+    int own = 0;
+    for (int k = lane; k < a.S; k += kWave) {
+        const ce_row_stats p = in[k];
+        if (p.m != ninf()) s += p.s * exp((double)p.m - M);
+        zt += (double)p.zt;
+        own += p.own;
+        sz += p.sz;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        s += __shfl_xor(s, o, kWave);
+        zt += __shfl_xor(zt, o, kWave);
+        sz += __shfl_xor(sz, o, kWave);
+        own += __shfl_xor(own, o, kWave);
+    }
+    if (lane != 0) return;
+    const int64_t t = a.target[r];
+    ce_row_final fo;
+    fo.lse = 0.0;
+    fo.gt = 0.0;
+    fo.m = 0.0f;
+    float loss;
+    if (t == a.ignore_index) {
+        fo.status = 0;
+        loss = 0.0f;
+    } else if (t < 0 || t >= a.V || own != 1) {
+        fo.status = -1;
+        loss = __builtin_nanf("");
+    } else {
+        const RowFinal f = finalize_row(M, s, zt, sz, (double)a.V, (double)a.eps);
+        fo.lse = f.lse;
+        fo.gt = f.gt;
+        fo.m = (float)M;
+        fo.status = 1;
+        loss = (float)f.loss;
+    }
+    a.fin[r] = fo;
+    a.loss_rows[r] = loss;
+}
+
 // zero-fill (a kernel rather than a memset node, so callers may capture it)
 __global__ __launch_bounds__(256) void k_zero_f32(float *p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -468,6 +537,12 @@ __global__ __launch_bounds__(256) void k_zero_f32(float *p, int64_t n) {
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+hipError_t launch_linear_merge(const LinMergeArgs &a, hipStream_t stream) {
+    const dim3 grid((unsigned)((a.N + kMergeWaves - 1) / kMergeWaves));
+    hipLaunchKernelGGL(k_linear_merge, grid, dim3(kMergeWaves * kWave), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t stream) {
     if (n <= 0) return hipSuccess;
     hipLaunchKernelGGL(k_zero_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, p, n);
