@@ -56,6 +56,9 @@ def assert_loss_rows(gpu_rows, ref, what=""):
     g = gpu_rows.detach().to("cpu").double().numpy()
     st = ref["status"]
     v = st == 1
+    inf = v & ~np.isfinite(ref["loss_rows"])   # e.g. -inf logits with smoothing: +inf
+    assert np.array_equal(g[inf], ref["loss_rows"][inf]), f"{what}: infinite per-row loss"
+    v = v & ~inf
     rel = np.abs(g[v] - ref["loss_rows"][v]) / np.maximum(np.abs(ref["loss_rows"][v]), 1e-300)
     assert rel.max(initial=0.0) <= LOSS_RTOL, f"{what}: per-row loss rel err {rel.max():.3e}"
     ign = st == 0

@@ -172,8 +172,11 @@ def _stats_check(gpu_stats, ref_stats, target, V_total, what, eps):
     assert rel.max(initial=0) <= 1e-5, f"{what}: s rel {rel.max():.2e}"
     if eps > 0:   # the row sum is only formed when smoothing needs it
         sz = ref_stats["sz"][read]
-        scale = np.maximum(np.abs(sz), 1.0)
-        assert (np.abs(st["sz"][read] - sz) / scale).max(initial=0) <= 1e-5, f"{what}: sum z"
+        gz = st["sz"][read]
+        fin = np.isfinite(sz)
+        assert np.array_equal(gz[~fin], sz[~fin]), f"{what}: infinite sum z"
+        scale = np.maximum(np.abs(sz[fin]), 1.0)
+        assert (np.abs(gz[fin] - sz[fin]) / scale).max(initial=0) <= 1e-5, f"{what}: sum z"
     skip = ~read
     assert np.all(st["m"][skip] == -np.inf) and np.all(st["s"][skip] == 0)
     assert np.all(st["own"][skip] == 0) and np.all(st["zt"][skip] == 0)
@@ -396,3 +399,45 @@ def test_writes_stay_inside_the_gradient_rows(T, V, in_dt, out_dt):
     ref = P.oracle_for(logits, target)
     P.assert_grad_close(out["grad"], ref["grad"], f"canary view T={T} V={V}")
     P.assert_loss_rows(out["loss_rows"], ref, "canary")
+
+
+@pytest.mark.parametrize("shard", [False, True])
+def test_smoothed_bf16_statistics_edge_values(shard):
+    """The smoothed bf16 statistics read e^z from a table of bf16 patterns
+    with 2^-16 <= |z| < 2^9: zeros and values below 2^-16 take a series,
+    values of magnitude >= 512 send the chunk to the online form, -inf
+    logits and the target read the table's zero entry."""
+    c, logits, target = _case(S.PAGE, 64, 5000, 131, eps=0.1)
+    z = logits.float().cpu()
+    t = target.cpu()
+    def put(r, cols, vals):
+        for col, v in zip(cols, vals):
+            if int(t[r]) != col:
+                z[r, col] = v
+    put(0, range(0, 400, 4), [0.0] * 100)
+    put(1, [3, 9, 27, 81, 243], [1e-6, -1e-6, 2.0 ** -16, -(2.0 ** -16), 3e-5])
+    put(2, [10], [600.0])
+    put(3, [20], [-700.0])
+    put(4, [5, 6], [-math.inf, -math.inf])
+    z[5] *= 1e-6
+    put(6, [30, 31, 32], [510.0, -510.0, 511.0])
+    put(7, [1, 2], [-1000.0, 1000.0])
+    logits = z.to(torch.bfloat16).to(DEV)
+    eps = 0.1
+    ref = P.oracle_for(logits, target, eps=eps)
+    if shard:
+        edges = [0, 2504, 5000]
+        stats = [vce.forward(logits[:, a:b], target, vocab_start=a, V_total=5000,
+                             label_smoothing=eps)["stats"] for a, b in zip(edges[:-1], edges[1:])]
+        m = vce.merge_shard_stats(stats, target, 5000, label_smoothing=eps)
+        fin, nv, lr = m["fin"], m["n_valid"], m["loss_rows"]
+    else:
+        f = vce.forward(logits, target, label_smoothing=eps)
+        fin, nv, lr = f["fin"], f["n_valid"], f["loss_rows"]
+        zz = to_numpy_logits(logits)
+        _stats_check(f["stats"], O.shard_stats(zz, t.numpy(), 0), t.numpy(), 5000,
+                     "table stats", eps)
+    g = vce.backward(logits, target, fin, nv, label_smoothing=eps)
+    torch.cuda.synchronize()
+    P.assert_loss_rows(lr, ref, "table edges")
+    P.assert_grad_close(g, ref["grad"], "table edges grad")

@@ -99,11 +99,12 @@ struct Layout {
     size_t fin;       // [T] ce_row_final
     size_t loss_rows; // [T] float
     size_t n_valid;   // [1] int32
+    size_t exp_tab;   // e^z table of the smoothed bf16 statistics
     size_t total;
 };
 
 Layout layout(const ce_problem *p, int op) {
-    Layout l{0, 0, 0, 0, 0};
+    Layout l{0, 0, 0, 0, 0, 0};
     const int64_t T = std::max<int64_t>(p->T, 0);
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -112,15 +113,18 @@ Layout layout(const ce_problem *p, int op) {
         return o;
     };
     const Plan pl = plan_chunks(T, p->V_local);
+    const size_t tab = p->label_smoothing > 0.0f ? (size_t)kExpTabN * sizeof(double) : 0;
     if (op == CE_OP_FORWARD) {
         l.partial = take(pl.nchunks > 1 ? (size_t)pl.nchunks * T * sizeof(ce_row_stats) : 0);
         l.loss_rows = take((size_t)T * sizeof(float));
         l.n_valid = take(sizeof(int32_t));
+        l.exp_tab = take(tab);
     } else if (op == CE_OP_FUSED) {
         l.partial = take((size_t)std::max(pl.nchunks, 1) * T * sizeof(ce_row_stats));
         l.fin = take((size_t)T * sizeof(ce_row_final));
         l.loss_rows = take((size_t)T * sizeof(float));
         l.n_valid = take(sizeof(int32_t));
+        l.exp_tab = take(tab);
     } else if (op == CE_OP_MERGE) {
         l.loss_rows = take((size_t)T * sizeof(float));
         l.n_valid = take(sizeof(int32_t));
@@ -267,7 +271,13 @@ int ce_forward(const ce_problem *prob, const void *logits, int logits_dtype,
     sa.chunk_cols = pl.chunk_cols;
     sa.out = pl.nchunks > 1 ? at<ce_row_stats>(ws, l.partial) : stats;
     sa.smoothing = p.label_smoothing > 0.0f;
+    sa.exp_tab = nullptr;
     const bool vec = vec_ok(logits, p.ld, logits_dtype, nullptr, 0, CE_F32);
+    if (sa.smoothing && vec && logits_dtype == CE_BF16) {
+        double *tab = at<double>(ws, l.exp_tab);
+        VCE_TRY(launch_exp_table(tab, s));
+        sa.exp_tab = tab;
+    }
     VCE_TRY(launch_stats(sa, logits_dtype, vec, s));
 
     MergeArgs ma;
@@ -429,6 +439,12 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
             sa.chunk_cols = pl.chunk_cols;
             sa.out = at<ce_row_stats>(ws, l.partial);
             sa.smoothing = p.label_smoothing > 0.0f;
+            sa.exp_tab = nullptr;
+            if (sa.smoothing && vec && logits_dtype == CE_BF16) {
+                double *tab = at<double>(ws, l.exp_tab);
+                VCE_TRY(launch_exp_table(tab, s));
+                sa.exp_tab = tab;
+            }
             VCE_TRY(launch_stats(sa, logits_dtype, vec, s));
 
             ce_row_final *fin = at<ce_row_final>(ws, l.fin);

@@ -579,42 +579,18 @@ struct Online<true> {
     __device__ __forceinline__ MaxSum result() const { return {m, s}; }
 };
 
+// Online (max, sum of exponentials) of the columns [c0, c1) of one row with
+// column tc (if in range) left out, and the sum of all of them (smoothing);
+// every thread of the workgroup calls it and gets the workgroup's result.
 template <int IN, int EPV, int THREADS, int UNROLL, bool LS>
-__global__ __launch_bounds__(THREADS) void k_stats(StatsArgs a) {
+__device__ __forceinline__ void stats_online(const char *zrow, int64_t c0, int64_t c1,
+                                             int64_t tc, BlockRed<THREADS> &red, MaxSum &ms_out,
+                                             double &sz_out) {
     using In = Elem<IN>;
     using Ch = Chunk<IN, EPV>;
-    __shared__ BlockRed<THREADS> red;
-
     const int tid = threadIdx.x;
-    const int64_t unit = xcd_major(blockIdx.x, gridDim.x);
-    const int64_t row = unit / a.nchunks;
-    const int ch = (int)(unit % a.nchunks);
-    const int64_t c0 = (int64_t)ch * a.chunk_cols;
-    const int64_t c1 = std::min(a.V_local, c0 + a.chunk_cols);
-    const int64_t t = a.target[row];
-    ce_row_stats *o = a.out + (int64_t)ch * a.T + row;
-
-    if (t == a.ignore_index || t < 0 || t >= a.V_total) {
-        // no row statistics are needed: the row is ignored or an error
-        if (tid == 0) {
-            ce_row_stats z;
-            z.m = ninf();
-            z.zt = 0.0f;
-            z.own = 0;
-            z.reserved = 0;
-            z.s = 0.0;
-            z.sz = 0.0;
-            *o = z;
-        }
-        return;
-    }
-    const int64_t tl = t - a.vocab_start; // target column in this call
-    const int64_t tc = (tl >= c0 && tl < c1) ? tl : -1;
-
-    const char *zrow = static_cast<const char *>(a.logits) + row * a.ld * In::kSize;
     const int64_t nv = (c1 - c0) / EPV; // full vectors of this chunk
     const int64_t tail0 = c0 + nv * EPV;
-
     Online<LS> acc;
     double sz = 0.0;
     for (int64_t base = 0; base < nv; base += (int64_t)UNROLL * THREADS) {
@@ -667,10 +643,249 @@ __global__ __launch_bounds__(THREADS) void k_stats(StatsArgs a) {
     }
     const MaxSum ms = block_combine<THREADS>(acc.result(), red);
     if (LS) sz = block_sum_d<THREADS>(sz, red, 1);
+    ms_out = ms;
+    sz_out = sz;
+}
+
+template <int IN, int EPV, int THREADS, int UNROLL, bool LS>
+__global__ __launch_bounds__(THREADS) void k_stats(StatsArgs a) {
+    using In = Elem<IN>;
+    using Ch = Chunk<IN, EPV>;
+    __shared__ BlockRed<THREADS> red;
+
+    const int tid = threadIdx.x;
+    const int64_t unit = xcd_major(blockIdx.x, gridDim.x);
+    const int64_t row = unit / a.nchunks;
+    const int ch = (int)(unit % a.nchunks);
+    const int64_t c0 = (int64_t)ch * a.chunk_cols;
+    const int64_t c1 = std::min(a.V_local, c0 + a.chunk_cols);
+    const int64_t t = a.target[row];
+    ce_row_stats *o = a.out + (int64_t)ch * a.T + row;
+
+    if (t == a.ignore_index || t < 0 || t >= a.V_total) {
+        // no row statistics are needed: the row is ignored or an error
+        if (tid == 0) {
+            ce_row_stats z;
+            z.m = ninf();
+            z.zt = 0.0f;
+            z.own = 0;
+            z.reserved = 0;
+            z.s = 0.0;
+            z.sz = 0.0;
+            *o = z;
+        }
+        return;
+    }
+    const int64_t tl = t - a.vocab_start; // target column in this call
+    const int64_t tc = (tl >= c0 && tl < c1) ? tl : -1;
+
+    const char *zrow = static_cast<const char *>(a.logits) + row * a.ld * In::kSize;
+    MaxSum ms;
+    double sz;
+    stats_online<IN, EPV, THREADS, UNROLL, LS>(zrow, c0, c1, tc, red, ms, sz);
     if (tid == 0) {
         ce_row_stats r;
         r.m = ms.m;
         r.zt = (tc >= 0) ? In::load1(zrow + tc * In::kSize) : 0.0f;
+        r.own = (tc >= 0) ? 1 : 0;
+        r.reserved = 0;
+        r.s = ms.s;
+        r.sz = sz;
+        *o = r;
+    }
+}
+
+// ===========================================================================
+// smoothed statistics of bf16 rows from a table of e^z
+// ===========================================================================
+// With smoothing the row sum must be fp64-exact (the gradient k (p - eps/V)
+// cancels near p = eps/V).  A bf16 logit is one of 65536 values; those with
+// 2^-16 <= |z| < 2^9 are 2 x 3200 bit patterns, whose e^z (fp64, from the
+// math library) make a 50 KB table in LDS.  The row sum is taken unshifted,
+// sum_j e^{z_j} (fp64 spans e^{-512} .. e^{512}), and scaled by e^{-m} at
+// the end: one LDS read and one fp64 add per element instead of an fp64
+// exponential.  The target and -inf logits read the table's zero entry.
+// |z| < 2^-16 takes e^z = 1 + z + z^2/2 (error below 1e-15); a chunk with
+// |z| >= 512, +inf or NaN is recomputed with the online form.
+
+__global__ __launch_bounds__(256) void k_exp_table(double *tab) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= kExpTabN) return;
+    if (i == kExpTabZero) {
+        tab[i] = 0.0;
+        return;
+    }
+    const uint32_t b = (kExpTabLo + (uint32_t)(i % kExpTabHalf)) | (i >= kExpTabHalf ? 0x8000u : 0u);
+    tab[i] = exp((double)__uint_as_float(b << 16));
+}
+
+template <int THREADS, int UNROLL>
+__global__ __launch_bounds__(THREADS) void k_stats_tab(StatsArgs a, const double *tab_g) {
+    using Ch = Chunk<CE_BF16, 8>;
+    __shared__ BlockRed<THREADS> red;
+    __shared__ double tab[kExpTabN];
+
+    const int tid = threadIdx.x;
+    const int64_t unit = xcd_major(blockIdx.x, gridDim.x);
+    const int64_t row = unit / a.nchunks;
+    const int ch = (int)(unit % a.nchunks);
+    const int64_t c0 = (int64_t)ch * a.chunk_cols;
+    const int64_t c1 = std::min(a.V_local, c0 + a.chunk_cols);
+    const int64_t t = a.target[row];
+    ce_row_stats *o = a.out + (int64_t)ch * a.T + row;
+
+    if (t == a.ignore_index || t < 0 || t >= a.V_total) {
+        if (tid == 0) {
+            ce_row_stats z;
+            z.m = ninf();
+            z.zt = 0.0f;
+            z.own = 0;
+            z.reserved = 0;
+            z.s = 0.0;
+            z.sz = 0.0;
+            *o = z;
+        }
+        return;
+    }
+    for (int i = tid; i < kExpTabN; i += THREADS) tab[i] = tab_g[i];
+    const int64_t tl = t - a.vocab_start;
+    const int64_t tc = (tl >= c0 && tl < c1) ? tl : -1;
+    const char *zrow = static_cast<const char *>(a.logits) + row * a.ld * 2;
+    const int64_t nv = (c1 - c0) / 8;
+    const int64_t tail0 = c0 + nv * 8;
+    __syncthreads();
+
+    // table index of one bf16 pattern; sets *rare when it is outside the table
+    // (the zero entry is read then, and the rare path below corrects it)
+    auto index = [&](uint32_t b, bool &rare) {
+        const uint32_t off = (b & 0x7fffu) - kExpTabLo;
+        const bool in = off < (uint32_t)kExpTabHalf;
+        rare |= !in;
+        return in ? (int)(off + (b >> 15) * kExpTabHalf) : kExpTabZero;
+    };
+    // the exact term of a pattern outside the table, and whether the online
+    // form is needed instead
+    auto rare_term = [&](uint32_t b, bool &redo) {
+        const uint32_t mag = b & 0x7fffu;
+        if (b == 0xff80u) return 0.0;                    // -inf (or the target)
+        if (mag < kExpTabLo) {                           // |z| < 2^-16, or 0
+            const double z = (double)__uint_as_float(b << 16);
+            return 1.0 + z * (1.0 + 0.5 * z);
+        }
+        if (mag < (uint32_t)(kExpTabLo + kExpTabHalf)) return 0.0; // in the table
+        redo = true;                                     // |z| >= 512, +inf, NaN
+        return 0.0;
+    };
+
+    double s = 0.0, sz = 0.0;
+    float mx = ninf();
+    bool redo = false;
+    // One vector of 8 logits.  The common path adds the table entries of all
+    // 8 and takes their max; a vector with a pattern outside the table, or
+    // holding the target, is redone element by element (the target left out).
+    auto vec = [&](const Ch &v, int64_t col) {
+        float zf[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) zf[e] = v.get(e);
+        float p[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) p[e] = zf[e];
+#pragma unroll
+        for (int hh = 4; hh > 0; hh >>= 1)
+#pragma unroll
+            for (int e = 0; e < hh; ++e) p[e] += p[e + hh];
+        sz += (double)p[0];
+        bool rare = tc >= col && tc < col + 8;
+        double sv = 0.0;
+        float vm = zf[0];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if (e) vm = fmaxf(vm, zf[e]);
+            const uint32_t w = v.v[e >> 1];
+            sv += tab[index((e & 1) ? (w >> 16) : (w & 0xffffu), rare)];
+        }
+        if (__builtin_expect(rare, 0)) {
+            sv = 0.0;
+            vm = ninf();
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                if (col + e == tc) continue;
+                const uint32_t w = v.v[e >> 1];
+                const uint32_t b = (e & 1) ? (w >> 16) : (w & 0xffffu);
+                bool r2 = false;
+                const double tv = tab[index(b, r2)];
+                sv += r2 ? rare_term(b, redo) : tv;
+                vm = fmaxf(vm, zf[e]);
+            }
+        }
+        s += sv;
+        mx = fmaxf(mx, vm);
+    };
+    const int64_t step = (int64_t)UNROLL * THREADS;
+    const int64_t nfull = nv / step * step; // vectors covered by whole iterations
+    // the next group's loads are issued before the current group's work
+    Ch va[UNROLL], vb[UNROLL];
+    auto load_group = [&](Ch *v, int64_t base) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+            v[u].load(zrow + (c0 + (base + (int64_t)u * THREADS + tid) * 8) * 2);
+    };
+    auto work_group = [&](Ch *v, int64_t base) {
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) vec(v[u], c0 + (base + (int64_t)u * THREADS + tid) * 8);
+    };
+    if (nfull > 0) load_group(va, 0);
+    for (int64_t base = 0; base < nfull; base += 2 * step) {
+        if (base + step < nfull) load_group(vb, base + step);
+        work_group(va, base);
+        if (base + step < nfull) {
+            if (base + 2 * step < nfull) load_group(va, base + 2 * step);
+            work_group(vb, base + step);
+        }
+    }
+    for (int64_t vi = nfull + tid; vi < nv; vi += THREADS) {
+        Ch v;
+        v.load(zrow + (c0 + vi * 8) * 2);
+        vec(v, c0 + vi * 8);
+    }
+    // scalar tail of the chunk
+    for (int64_t col = tail0 + tid; col < c1; col += THREADS) {
+        const uint32_t b = *reinterpret_cast<const uint16_t *>(zrow + col * 2);
+        const float z = __uint_as_float(b << 16);
+        sz += (double)z;
+        if (col == tc) continue;
+        mx = fmaxf(mx, z);
+        bool rare = false;
+        const double tv = tab[index(b, rare)];
+        s += rare ? rare_term(b, redo) : tv;
+    }
+    // a thread that saw |z| >= 512, +inf or NaN sends the chunk to the online form
+    const float redo_all = block_max<THREADS>(redo ? 1.0f : 0.0f, red, 0);
+    MaxSum ms;
+    if (redo_all > 0.0f) {
+        __syncthreads();
+        stats_online<CE_BF16, 8, THREADS, UNROLL, true>(zrow, c0, c1, tc, red, ms, sz);
+    } else {
+        const float M = block_max<THREADS>(mx, red, 1);
+        __syncthreads();
+        const double S = block_sum_d<THREADS>(s, red, 0);
+        sz = block_sum_d<THREADS>(sz, red, 1);
+        // e^{-M}: -M is a bf16 value (M is a max of bf16 values)
+        double scale = 0.0;
+        if (M != ninf()) {
+            const uint32_t mb = (__float_as_uint(M) >> 16) ^ 0x8000u;
+            bool rare = false;
+            bool unused = false;
+            const double tv = tab[index(mb, rare)];
+            scale = rare ? rare_term(mb, unused) : tv;
+        }
+        ms.m = M;
+        ms.s = (M == ninf()) ? 0.0 : S * scale;
+    }
+    if (tid == 0) {
+        ce_row_stats r;
+        r.m = ms.m;
+        r.zt = (tc >= 0) ? __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t *>(zrow + tc * 2)) << 16) : 0.0f;
         r.own = (tc >= 0) ? 1 : 0;
         r.reserved = 0;
         r.s = ms.s;
@@ -940,9 +1155,19 @@ static void stats_dispatch(const StatsArgs &a, bool vec, dim3 grid, hipStream_t 
                            0, stream, a);
 }
 
+hipError_t launch_exp_table(double *tab, hipStream_t stream) {
+    hipLaunchKernelGGL(k_exp_table, dim3((kExpTabN + 255) / 256), dim3(256), 0, stream, tab);
+    return hipGetLastError();
+}
+
 hipError_t launch_stats(const StatsArgs &a, int in_dt, bool vec, hipStream_t stream) {
     const dim3 grid((unsigned)(a.T * a.nchunks));
     const bool ls = a.smoothing != 0;
+    if (ls && vec && in_dt == CE_BF16 && a.exp_tab) {
+        hipLaunchKernelGGL((k_stats_tab<kStreamThreads, kStreamUnroll>), grid,
+                           dim3(kStreamThreads), 0, stream, a, a.exp_tab);
+        return hipGetLastError();
+    }
     if (in_dt == CE_BF16)
         ls ? stats_dispatch<CE_BF16, true>(a, vec, grid, stream)
            : stats_dispatch<CE_BF16, false>(a, vec, grid, stream);

@@ -37,7 +37,15 @@ struct StatsArgs {
     int64_t chunk_cols;   // columns per chunk (multiple of the vector width)
     ce_row_stats *out;    // [nchunks][T]
     int smoothing;        // label smoothing on: fp64 sums, and the row sum of z
+    const double *exp_tab; // smoothing, bf16 rows: e^z per bf16 pattern (kExpTabN), or NULL
 };
+
+// Table of e^z for the bf16 patterns with 2^-16 <= |z| < 2^9 (both signs),
+// plus one zero entry, used by the smoothed statistics of bf16 rows.
+constexpr uint32_t kExpTabLo = 0x3780; // bf16 bits of 2^-16
+constexpr int kExpTabHalf = 3200;      // patterns per sign up to 2^9
+constexpr int kExpTabZero = 2 * kExpTabHalf;
+constexpr int kExpTabN = 2 * kExpTabHalf + 1;
 
 struct MergeArgs {
     const ce_row_stats *in; // [S][T]
@@ -149,6 +157,7 @@ hipError_t launch_fused_resident(const FusedArgs &a, int in_dt, int out_dt, int6
 // vec: 16-byte vectors (rows aligned) rather than single elements
 hipError_t launch_stats(const StatsArgs &a, int in_dt, bool vec, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
+hipError_t launch_exp_table(double *tab, hipStream_t stream);
 hipError_t launch_grad(const GradArgs &a, int in_dt, int out_dt, bool vec, int64_t T,
                        hipStream_t stream);
 
