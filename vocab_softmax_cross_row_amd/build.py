@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libvocab_ce.so")
-SOURCES = [os.path.join(CSRC, f) for f in ("ce_kernels.hip", "ce_linear.hip", "ce_api.hip")]
+SOURCES = [os.path.join(CSRC, f) for f in ("ce_kernels.hip", "ce_fused.hip", "ce_linear.hip", "ce_api.hip")]
 ARCH = "gfx950"
 
 

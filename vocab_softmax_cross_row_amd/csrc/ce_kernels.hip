@@ -1,22 +1,17 @@
-// Cross-entropy kernels for gfx950 and the C ABI declared in vocab_ce.h.
+// Cross-entropy kernels for gfx950: the streaming paths and the counts.
 //
-// Paths
-//   fused, row resident: one workgroup per row holds the whole row in
-//     registers (16-byte vectors, up to 16 per thread), so the logits are
-//     read from HBM once and the gradient written once: a max sweep, a
-//     sum-of-exponentials sweep, an fp64 finalize by one thread, then the
-//     gradient sweep, all from registers (torchtitan PR "[loss] fix softmax
-//     collapse with improved ce perf", Memory/perf: one read of the logits,
-//     the backward rebuilt in one fused pass).
-//   streaming: the stats kernel (one read, online max / sum per thread),
-//     the finalize kernel (merge of column-chunk or shard statistics, fp64
-//     finalize) and the gradient kernel (one read, one write).  They serve
-//     ce_forward / ce_merge_shard_stats / ce_backward, and the fused entry
-//     point when the row does not fit in registers, when rows are not
-//     16-byte aligned, or when there are too few rows to fill the GPU (then
-//     each row is split into column chunks: the split-V grid).
+//   streaming: the stats kernel (one read, online max / sum per thread, or
+//     the e^z table for smoothed bf16 rows), the merge kernel (column-chunk
+//     or shard statistics, fp64 finalize) and the gradient kernel (one
+//     read, one write).  They serve ce_forward / ce_merge_shard_stats /
+//     ce_backward, and the fused entry point when the row does not fit on
+//     chip, when rows are not 16-byte aligned, or when there are too few
+//     rows to fill the GPU (then each row is split into column chunks: the
+//     split-V grid).
 //   count and reduce: N_valid / bad-target counts before the gradient needs
 //     them, and the deterministic loss sum.
+//
+// The fused, row-resident kernels are in ce_fused.hip.
 
 #include <hip/hip_runtime.h>
 
@@ -103,433 +98,6 @@ __global__ __launch_bounds__(kReduceThreads) void k_reduce(const float *__restri
     if (threadIdx.x == 0) {
         if (reduction == CE_RED_MEAN) acc /= (double)(*n_valid);
         *loss = (float)acc;
-    }
-}
-
-// ===========================================================================
-// fused, row resident
-// ===========================================================================
-
-// One workgroup per row; the row lives in registers from its load to its
-// gradient store.  FAST = bf16 gradient without smoothing: fp32 finalize
-// and the biased exponent form (see GradConst); otherwise fp64 finalize.
-template <int IN, int OUT, int THREADS, int NV, bool LS>
-__global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
-    using In = Elem<IN>;
-    constexpr int EPV = In::kVec;
-    using Ch = Chunk<IN, EPV>;
-    using St = Store<OUT, EPV, true>;
-    constexpr int kOutSize = (OUT == CE_BF16) ? 2 : 4;
-    constexpr bool FAST = (OUT == CE_BF16) && !LS;
-
-    __shared__ BlockRed<THREADS> red;
-    __shared__ GradConst gc_sh;
-
-    const int tid = threadIdx.x;
-    const int64_t row = xcd_major(blockIdx.x, gridDim.x);
-    const int V = (int)a.V;
-    const int nvec = V / EPV;
-    const int tail0 = nvec * EPV;
-    const int ntail = V - tail0;
-    const char *zrow = static_cast<const char *>(a.logits) + row * a.ld * In::kSize;
-    char *grow = static_cast<char *>(a.grad) + row * a.ldg * kOutSize;
-
-    const int64_t t64 = a.target[row];
-    if (t64 == a.ignore_index || t64 < 0 || t64 >= V) {
-        // ignored row or bad target: zero gradient, no reads of the row
-        float zero[EPV];
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) zero[e] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int vi = i * THREADS + tid;
-            if (vi < nvec) St::put(grow + vi * EPV * kOutSize, zero);
-        }
-        if (tid < ntail) Store<OUT, 1>::put(grow + (tail0 + tid) * kOutSize, zero);
-        if (tid == 0) a.loss_rows[row] = (t64 == a.ignore_index) ? 0.0f : __builtin_nanf("");
-        return;
-    }
-    const int t = (int)t64;
-
-    // ---- load the row into registers (streamed: read once) ----------------
-    Ch v[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int vi = i * THREADS + tid;
-        if (vi < nvec)
-            v[i].template load<true>(zrow + vi * EPV * In::kSize);
-        else
-            v[i].fill_ninf();
-    }
-    float ztail = ninf();
-    if (tid < ntail) ztail = In::load1(zrow + (tail0 + tid) * In::kSize);
-
-    // where the target sits: vector tv = slot t_slot of thread t_thread
-    // (wave t_wave), element te; or the scalar tail.  t is the same for the
-    // whole workgroup, and readfirstlane makes the slot and wave tests
-    // scalar branches, so only the owner wave does any work for it.
-    const int tv = t / EPV;
-    const int te = __builtin_amdgcn_readfirstlane(t - tv * EPV);
-    const bool t_in_vec = t < tail0;
-    const int t_slot = __builtin_amdgcn_readfirstlane(t_in_vec ? tv / THREADS : -1);
-    const int t_thread = tv - (tv / THREADS) * THREADS;
-    const int t_wave = __builtin_amdgcn_readfirstlane(t_thread / kWave);
-    const int my_wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const bool t_wave_mine = t_in_vec && my_wave == t_wave;
-    const bool t_lane_mine = (tid & (kWave - 1)) == (t_thread & (kWave - 1));
-
-    // ---- sum of the whole row (smoothing only), before the target is masked
-    double sz = 0.0;
-    if constexpr (LS) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int vi = i * THREADS + tid;
-            float p[EPV];
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) p[e] = v[i].get(e);
-#pragma unroll
-            for (int h = EPV / 2; h > 0; h >>= 1)
-#pragma unroll
-                for (int e = 0; e < h; ++e) p[e] += p[e + h];
-            sz += (vi < nvec) ? (double)p[0] : 0.0;
-        }
-        if (tid < ntail) sz += (double)ztail;
-    }
-
-    // ---- drop the target before any reduction ------------------------------
-    if (t_wave_mine) {
-#pragma unroll
-        for (int i = 0; i < NV; ++i)
-            if (i == t_slot && t_lane_mine) v[i].kill(te);
-    }
-    if (!t_in_vec && tid == t - tail0) ztail = ninf();
-
-#pragma unroll
-    for (int i = 0; i < NV; ++i) v[i].fence();
-
-    // ---- non-target max ---------------------------------------------------
-    float mx = ztail;
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) mx = fmaxf(mx, v[i].get(e));
-    mx = block_max<THREADS>(mx, red, 0);
-#pragma unroll
-    for (int i = 0; i < NV; ++i) v[i].fence();
-
-    // ---- non-target sum of exponentials ----------------------------------
-    double sd = 0.0;
-    float s = 0.0f;
-    if constexpr (LS) {
-        // With smoothing the gradient k (p_j - eps/V) cancels where p_j is
-        // close to eps/V and magnifies any error of lse there, so the sum is
-        // taken with fp64 exponentials and fp64 accumulation.
-        if (mx != ninf()) {
-            const double md = (double)mx;
-#pragma unroll
-            for (int i = 0; i < NV; ++i)
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) sd += exp_nonpos((double)v[i].get(e) - md);
-            sd += exp_nonpos((double)ztail - md);
-        }
-        sd = block_sum_d<THREADS>(sd, red, 0);
-        sz = block_sum_d<THREADS>(sz, red, 1);
-    } else {
-        if (mx != ninf()) {
-            const float K = mx * kL2E;
-#pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                float p[EPV];
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) p[e] = fast_exp2(fmaf(v[i].get(e), kL2E, -K));
-#pragma unroll
-                for (int h = EPV / 2; h > 0; h >>= 1)
-#pragma unroll
-                    for (int e = 0; e < h; ++e) p[e] += p[e + h];
-                s += p[0];
-            }
-            s += fast_exp2(fmaf(ztail, kL2E, -K));
-        }
-        s = block_sum<THREADS>(s, red, 1);
-        if (mx != ninf()) {
-            // the terms were 2^(z kL2E - K) with K = fl(mx kL2E): undo the
-            // rounding of K (the residual is exact)
-            const float K = mx * kL2E;
-            s *= fast_exp2(-fmaf(mx, kL2E, -K));
-        }
-        sd = (double)s;
-    }
-
-    // ---- finalize (one thread) -----------------------------------------------
-    if (tid == 0) {
-        const float zt = In::load1(zrow + (int64_t)t * In::kSize);
-        const double k = row_scale(a.reduction, a.grad_output, a.n_valid, row);
-        if constexpr (FAST) {
-            const FastFinal f = finalize_fast(mx, s, zt, k);
-            a.loss_rows[row] = f.loss;
-            GradConst c;
-            c.cb = f.cb;
-            c.scale = f.scale;
-            c.gk = f.gk;
-            c.ch = c.cl = c.k = c.ku = c.lu = c.d2hi = c.d2lo = 0.0f;
-            gc_sh = c;
-        } else {
-            const RowFinal f =
-                finalize_row((double)mx, sd, (double)zt, sz, (double)V, (double)a.eps);
-            a.loss_rows[row] = (float)f.loss;
-            gc_sh = grad_constants(f.lse, f.gt, k, (double)a.eps, (double)V);
-        }
-    }
-    __syncthreads();
-    const GradConst c = gc_sh;
-#pragma unroll
-    for (int i = 0; i < NV; ++i) v[i].fence();
-
-    // ---- gradient sweep from registers ------------------------------------
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-        const int vi = i * THREADS + tid;
-        float g[EPV];
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) g[e] = grad_elem<OUT, LS>(v[i].get(e), c);
-        if (t_wave_mine && i == t_slot) {
-            if (t_lane_mine) {
-#pragma unroll
-                for (int e = 0; e < EPV; ++e)
-                    if (e == te) g[e] = c.gk;
-            }
-        }
-        if (vi < nvec) St::put(grow + vi * EPV * kOutSize, g);
-    }
-    if (tid < ntail) {
-        const float g = (!t_in_vec && tid == t - tail0) ? c.gk : grad_elem<OUT, LS>(ztail, c);
-        Store<OUT, 1>::put(grow + (tail0 + tid) * kOutSize, &g);
-    }
-}
-
-// ===========================================================================
-// fused, row split between registers and LDS, two workgroups per CU
-// ===========================================================================
-// For rows of more than 8192 16-byte vectors (V > 65536 bf16) a register-
-// resident row needs 1024 threads and fills the register file, so each CU
-// holds one row and its barriers, finalize and exponentials cannot overlap
-// another row's memory traffic.  Here a 512-thread workgroup keeps NR
-// vectors per lane in registers and the rest of the row in LDS (filled by
-// direct buffer->LDS loads), and two workgroups share a CU.  Buffer
-// addressing keeps every slot at one VGPR offset; the SGPR slot offset is
-// not covered by the buffer range check, so every possibly partial slot is
-// guarded explicitly.
-constexpr int kLdsThreads = 512;
-constexpr int kLdsRegSlots = 22;
-constexpr int kBufNT = 2; // buffer cache policy: non-temporal
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-template <int IN, int OUT, int NR>
-__global__ __launch_bounds__(kLdsThreads) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void k_fused_lds(FusedArgs a) {
-    using In = Elem<IN>;
-    constexpr int TH = kLdsThreads;
-    constexpr int EPV = In::kVec;
-    using Ch = Chunk<IN, EPV>;
-    constexpr int kOutSize = (OUT == CE_BF16) ? 2 : 4;
-    constexpr int kOutVec = EPV * kOutSize; // bytes of one gradient vector
-    constexpr bool FAST = (OUT == CE_BF16);
-    extern __shared__ u32x4 lbuf[];
-    __shared__ BlockRed<TH> red;
-    __shared__ GradConst gc_sh;
-
-    const int tid = threadIdx.x;
-    const int64_t row = xcd_major(blockIdx.x, gridDim.x);
-    const int V = (int)a.V;
-    const int nvec = V / EPV;
-    const int tail0 = nvec * EPV;
-    const int ntail = V - tail0;
-    const int nl = (nvec - NR * TH + TH - 1) / TH; // LDS slots (last one partial)
-    const char *zrow = static_cast<const char *>(a.logits) + row * a.ld * In::kSize;
-    char *grow = static_cast<char *>(a.grad) + row * a.ldg * kOutSize;
-    const __amdgpu_buffer_rsrc_t rin =
-        __builtin_amdgcn_make_buffer_rsrc((void *)zrow, 0, tail0 * In::kSize, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rout =
-        __builtin_amdgcn_make_buffer_rsrc((void *)grow, 0, tail0 * kOutSize, 0x00020000);
-    const int voff = tid * 16;
-    const int goff = tid * kOutVec;
-
-    auto put = [&](int slot, const float *g) {
-        if (slot * TH + tid >= nvec) return;
-        if constexpr (OUT == CE_BF16 && EPV == 8) {
-            u32x4 o;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) o[k] = pack_bf16x2(g[2 * k], g[2 * k + 1]);
-            __builtin_amdgcn_raw_buffer_store_b128(o, rout, goff, slot * TH * kOutVec, kBufNT);
-        } else if constexpr (OUT == CE_F32 && EPV == 4) {
-            u32x4 o;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) o[k] = __float_as_uint(g[k]);
-            __builtin_amdgcn_raw_buffer_store_b128(o, rout, goff, slot * TH * kOutVec, kBufNT);
-        } else {
-            Store<OUT, EPV, true>::put(grow + (int64_t)(slot * TH + tid) * kOutVec, g);
-        }
-    };
-
-    const int64_t t64 = a.target[row];
-    if (t64 == a.ignore_index || t64 < 0 || t64 >= V) {
-        float zero[EPV];
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) zero[e] = 0.0f;
-#pragma unroll
-        for (int i = 0; i < NR; ++i) put(i, zero);
-        for (int q = 0; q < nl; ++q) put(NR + q, zero);
-        if (tid < ntail) Store<OUT, 1>::put(grow + (tail0 + tid) * kOutSize, zero);
-        if (tid == 0) a.loss_rows[row] = (t64 == a.ignore_index) ? 0.0f : __builtin_nanf("");
-        return;
-    }
-    const int t = (int)t64;
-
-    // ---- loads: register slots first (needed first), then the LDS part.
-    // While a wave issues memory instructions it runs at raised priority, so
-    // the other workgroup's arithmetic on this CU does not delay the requests.
-    __builtin_amdgcn_s_setprio(1);
-    Ch v[NR];
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-        if (i * TH + tid < nvec)
-            v[i].v = __builtin_amdgcn_raw_buffer_load_b128(rin, voff, i * TH * 16, kBufNT);
-        else
-            v[i].fill_ninf();
-    }
-    const int wave_base = __builtin_amdgcn_readfirstlane((tid / kWave) * kWave);
-    for (int q = 0; q < nl; ++q)
-        if ((NR + q) * TH + tid < nvec)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rin, (lds_void_t *)(lbuf + q * TH + wave_base),
-                                                     16, voff, (NR + q) * TH * 16, 0, kBufNT);
-    float ztail = ninf();
-    if (tid < ntail) ztail = In::load1(zrow + (tail0 + tid) * In::kSize);
-    __builtin_amdgcn_s_setprio(0);
-
-    // ---- target location (wave-uniform tests; see k_fused_resident) ----------
-    const int tv = t / EPV;
-    const int te = __builtin_amdgcn_readfirstlane(t - tv * EPV);
-    const bool t_in_vec = t < tail0;
-    const int t_slot = __builtin_amdgcn_readfirstlane(t_in_vec ? tv / TH : -1);
-    const int t_thread = tv - (tv / TH) * TH;
-    const int t_wave = __builtin_amdgcn_readfirstlane(t_thread / kWave);
-    const int my_wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const bool t_wave_mine = t_in_vec && my_wave == t_wave;
-    const bool t_lane_mine = (tid & (kWave - 1)) == (t_thread & (kWave - 1));
-
-    if (t_wave_mine) {
-#pragma unroll
-        for (int i = 0; i < NR; ++i)
-            if (i == t_slot && t_lane_mine) v[i].kill(te);
-    }
-    if (!t_in_vec && tid == t - tail0) ztail = ninf();
-#pragma unroll
-    for (int i = 0; i < NR; ++i) v[i].fence();
-
-    // ---- non-target max: registers, then (once this wave's LDS part has
-    // landed) the LDS slots; each lane reads back only what it loaded ----
-    float mx = ztail;
-#pragma unroll
-    for (int i = 0; i < NR; ++i)
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) mx = fmaxf(mx, v[i].get(e));
-    __builtin_amdgcn_s_waitcnt(0);
-    if (t_wave_mine && t_slot >= NR && t_lane_mine) {
-        Ch w;
-        w.v = lbuf[(t_slot - NR) * TH + tid];
-        w.kill(te);
-        lbuf[(t_slot - NR) * TH + tid] = w.v;
-    }
-    auto lds_vec = [&](int q) {
-        Ch w;
-        if ((NR + q) * TH + tid < nvec)
-            w.v = lbuf[q * TH + tid];
-        else
-            w.fill_ninf();
-        return w;
-    };
-#pragma unroll 1
-    for (int q = 0; q < nl; ++q) {
-        const Ch w = lds_vec(q);
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) mx = fmaxf(mx, w.get(e));
-    }
-    mx = block_max<TH>(mx, red, 0);
-#pragma unroll
-    for (int i = 0; i < NR; ++i) v[i].fence();
-
-    // ---- non-target sum of exponentials ----------------------------------
-    float s = 0.0f;
-    if (mx != ninf()) {
-        const float K = mx * kL2E;
-        auto sumvec = [&](const Ch &w) {
-            float p[EPV];
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) p[e] = fast_exp2(fmaf(w.get(e), kL2E, -K));
-#pragma unroll
-            for (int h = EPV / 2; h > 0; h >>= 1)
-#pragma unroll
-                for (int e = 0; e < h; ++e) p[e] += p[e + h];
-            s += p[0];
-        };
-#pragma unroll
-        for (int i = 0; i < NR; ++i) sumvec(v[i]);
-#pragma unroll 1
-        for (int q = 0; q < nl; ++q) sumvec(lds_vec(q));
-        s += fast_exp2(fmaf(ztail, kL2E, -K));
-    }
-    s = block_sum<TH>(s, red, 1);
-    if (mx != ninf()) {
-        const float K = mx * kL2E;
-        s *= fast_exp2(-fmaf(mx, kL2E, -K));
-    }
-
-    // ---- finalize (one thread) ---------------------------------------------
-    if (tid == 0) {
-        const float zt = In::load1(zrow + (int64_t)t * In::kSize);
-        const double k = row_scale(a.reduction, a.grad_output, a.n_valid, row);
-        if constexpr (FAST) {
-            const FastFinal f = finalize_fast(mx, s, zt, k);
-            a.loss_rows[row] = f.loss;
-            GradConst c;
-            c.cb = f.cb;
-            c.scale = f.scale;
-            c.gk = f.gk;
-            c.ch = c.cl = c.k = c.ku = c.lu = c.d2hi = c.d2lo = 0.0f;
-            gc_sh = c;
-        } else {
-            const RowFinal f = finalize_row((double)mx, (double)s, (double)zt, 0.0, (double)V, 0.0);
-            a.loss_rows[row] = (float)f.loss;
-            gc_sh = grad_constants(f.lse, f.gt, k, 0.0, (double)V);
-        }
-    }
-    __syncthreads();
-    const GradConst c = gc_sh;
-#pragma unroll
-    for (int i = 0; i < NR; ++i) v[i].fence();
-
-    // ---- gradient sweep -----------------------------------------------------
-    auto gradvec = [&](const Ch &w, int slot) {
-        float g[EPV];
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) g[e] = grad_elem<OUT, false>(w.get(e), c);
-        if (t_wave_mine && slot == t_slot) {
-            if (t_lane_mine) {
-#pragma unroll
-                for (int e = 0; e < EPV; ++e)
-                    if (e == te) g[e] = c.gk;
-            }
-        }
-        put(slot, g);
-    };
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int i = 0; i < NR; ++i) gradvec(v[i], i);
-#pragma unroll 1
-    for (int q = 0; q < nl; ++q) gradvec(lds_vec(q), NR + q);
-    if (tid < ntail) {
-        const float g = (!t_in_vec && tid == t - tail0) ? c.gk : grad_elem<OUT, false>(ztail, c);
-        Store<OUT, 1>::put(grow + (tail0 + tid) * kOutSize, &g);
     }
 }
 
@@ -1043,102 +611,6 @@ hipError_t launch_reduce(const float *loss_rows, int64_t T, int reduction, const
     hipLaunchKernelGGL(k_reduce, dim3(1), dim3(kReduceThreads), 0, stream, loss_rows, T,
                        reduction, n_valid, loss);
     return hipGetLastError();
-}
-
-// (threads, vectors per thread) of the row-resident kernel, smallest first
-struct ResidentShape {
-    int threads, nv;
-};
-constexpr ResidentShape kResident[] = {{256, 1}, {256, 2},  {256, 4},  {256, 8},
-                                       {256, 16}, {512, 16}, {1024, 16}};
-
-static int resident_index(int in_dt, int64_t V) {
-    const int64_t epv = (in_dt == CE_BF16) ? 8 : 4;
-    const int64_t nvec = V / epv;
-    for (int i = 0; i < (int)(sizeof(kResident) / sizeof(kResident[0])); ++i)
-        if ((int64_t)kResident[i].threads * kResident[i].nv >= nvec &&
-            kResident[i].threads >= V - nvec * epv)
-            return i;
-    return -1;
-}
-
-int resident_threads(int in_dt, int64_t V) {
-    const int i = resident_index(in_dt, V);
-    return i < 0 ? 0 : kResident[i].threads;
-}
-
-template <int IN, int OUT, bool LS>
-static hipError_t fused_dispatch(const FusedArgs &a, int64_t T, hipStream_t stream) {
-    const int i = resident_index(IN, a.V);
-    const dim3 grid((unsigned)T);
-#define VCE_RES(TH, NV)                                                                         \
-    hipLaunchKernelGGL((k_fused_resident<IN, OUT, TH, NV, LS>), grid, dim3(TH), 0, stream, a); \
-    break;
-    switch (i) {
-    case 0: VCE_RES(256, 1)
-    case 1: VCE_RES(256, 2)
-    case 2: VCE_RES(256, 4)
-    case 3: VCE_RES(256, 8)
-    case 4: VCE_RES(256, 16)
-    case 5: VCE_RES(512, 16)
-    case 6: VCE_RES(1024, 16)
-    default: return hipErrorInvalidValue;
-    }
-#undef VCE_RES
-    return hipGetLastError();
-}
-
-// LDS bytes per workgroup the split kernel needs for V columns (0 if the
-// row is not in its range).
-static int lds_split_bytes(int in_dt, int64_t V) {
-    const int64_t epv = (in_dt == CE_BF16) ? 8 : 4;
-    const int64_t nvec = V / epv;
-    const int64_t reg = (int64_t)kLdsRegSlots * kLdsThreads;
-    if (nvec <= 8192 || nvec <= reg) return 0;
-    const int64_t bytes = (nvec - reg) * 16;
-    // two workgroups per CU: half of the 160 KB LDS each, less the static part
-    if (bytes > 163840 / 2 - 512) return 0;
-    return (int)bytes;
-}
-
-template <int IN, int OUT>
-static hipError_t launch_lds(const FusedArgs &a, int64_t T, int lds, hipStream_t stream) {
-    static bool configured = false;
-    if (!configured) {
-        const hipError_t e = hipFuncSetAttribute(
-            (const void *)k_fused_lds<IN, OUT, kLdsRegSlots>,
-            hipFuncAttributeMaxDynamicSharedMemorySize, 163840 / 2 - 512);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
-    hipLaunchKernelGGL((k_fused_lds<IN, OUT, kLdsRegSlots>), dim3((unsigned)T), dim3(kLdsThreads),
-                       lds, stream, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_fused_resident(const FusedArgs &a, int in_dt, int out_dt, int64_t T,
-                                 hipStream_t stream) {
-    const bool ls = a.eps > 0.0f;
-    const int lds = ls ? 0 : lds_split_bytes(in_dt, a.V);
-    if (lds > 0) {
-        if (in_dt == CE_BF16)
-            return out_dt == CE_BF16 ? launch_lds<CE_BF16, CE_BF16>(a, T, lds, stream)
-                                     : launch_lds<CE_BF16, CE_F32>(a, T, lds, stream);
-        return out_dt == CE_BF16 ? launch_lds<CE_F32, CE_BF16>(a, T, lds, stream)
-                                 : launch_lds<CE_F32, CE_F32>(a, T, lds, stream);
-    }
-    if (in_dt == CE_BF16) {
-        if (out_dt == CE_BF16)
-            return ls ? fused_dispatch<CE_BF16, CE_BF16, true>(a, T, stream)
-                      : fused_dispatch<CE_BF16, CE_BF16, false>(a, T, stream);
-        return ls ? fused_dispatch<CE_BF16, CE_F32, true>(a, T, stream)
-                  : fused_dispatch<CE_BF16, CE_F32, false>(a, T, stream);
-    }
-    if (out_dt == CE_BF16)
-        return ls ? fused_dispatch<CE_F32, CE_BF16, true>(a, T, stream)
-                  : fused_dispatch<CE_F32, CE_BF16, false>(a, T, stream);
-    return ls ? fused_dispatch<CE_F32, CE_F32, true>(a, T, stream)
-              : fused_dispatch<CE_F32, CE_F32, false>(a, T, stream);
 }
 
 constexpr int kStreamThreads = 256;
