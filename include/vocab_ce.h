@@ -39,8 +39,12 @@
  *     caller owns and allocates every buffer; the library never allocates,
  *     frees or synchronises, and launches all work on `stream` (a
  *     hipStream_t; NULL is the default stream).  Calls are asynchronous.
- *   - Inputs are const and never written.  Outputs must not overlap inputs
- *     or each other.
+ *   - Inputs are const and never written, with one opt-in exception: the
+ *     gradient may be written in place over the logits (grad == logits,
+ *     ldg == ld, grad_dtype == logits_dtype), as the torchtitan PR's eager
+ *     path and Megatron-core's in-place methods do, halving the memory of a
+ *     fused step.  Any other overlap of outputs with inputs or with each
+ *     other is an error.
  *   - Logits: row r, column j of this call lives at logits[r * ld + j]
  *     (elements, not bytes), j in [0, V_local).  Any alignment is accepted;
  *     16-byte aligned rows take the vectorised path.
@@ -89,7 +93,7 @@ typedef enum {
     CE_ERR_REDUCTION = -5, /* unknown ce_reduction */
     CE_ERR_WORKSPACE = -6, /* workspace NULL or smaller than ce_workspace_bytes */
     CE_ERR_SHARDS = -7,    /* n_shards < 1 or > CE_MAX_SHARDS */
-    CE_ERR_ALIAS = -8,     /* grad overlaps logits */
+    CE_ERR_ALIAS = -8,     /* grad overlaps logits other than exactly in place */
     CE_ERR_HIP = -9,       /* a HIP launch failed */
     CE_ERR_ARG = -10       /* an output given where the call cannot produce it
                               (e.g. finalize outputs of a split-vocabulary
@@ -186,7 +190,9 @@ int ce_merge_shard_stats(const ce_problem *prob, int n_shards,
  *   grad_output device float: [1] for sum and mean, [T] for none; NULL
  *               means 1.0 everywhere.
  *   grad        [T, V_local] out, row stride ldg elements, grad_dtype;
- *               must not overlap the logits (CE_ERR_ALIAS).
+ *               may be the logits themselves (same pointer, ldg == ld,
+ *               same dtype: the gradient overwrites them); any other
+ *               overlap is CE_ERR_ALIAS.
  * Ignored and bad-target rows get +0 everywhere.
  * Megatron-core VocabParallelCrossEntropy.prepare_gradient_calculation_operands,
  * calculate_gradients, scale_gradients_inplace; torchtitan PR Numerics

@@ -130,3 +130,25 @@ def test_linear_null_and_pairing_checks(lib):
     # misaligned E
     assert lib.ce_linear_fwd_bwd(ctypes.byref(p), ctypes.c_void_p(258), one, one, None, None,
                                  None, None, None, None, None, one, ws, None) == -2
+
+
+def test_alias_checks_before_any_launch(lib):
+    """grad may be the logits exactly (same pointer, stride and dtype: an
+    in-place gradient); any other overlap is CE_ERR_ALIAS, found on the host."""
+    p = B.make_problem(4, 10, 16)
+    ws_bytes = B.ce_workspace_bytes(p, B.CE_OP_FUSED)
+    base = 1 << 20
+    ws = ctypes.c_void_p(1 << 30)
+    one = ctypes.c_void_p(256)
+    # overlapping by two bytes
+    rc = lib.ce_fused_fwd_bwd(ctypes.byref(p), ctypes.c_void_p(base), 1, one, None, None, None,
+                              None, None, ctypes.c_void_p(base + 2), 1, 16, ws, ws_bytes, None)
+    assert rc == -8
+    # same pointer, other stride
+    rc = lib.ce_fused_fwd_bwd(ctypes.byref(p), ctypes.c_void_p(base), 1, one, None, None, None,
+                              None, None, ctypes.c_void_p(base), 1, 20, ws, ws_bytes, None)
+    assert rc == -8
+    # same pointer, other dtype
+    rc = lib.ce_backward(ctypes.byref(p), ctypes.c_void_p(base), 1, one, one, one, None,
+                         ctypes.c_void_p(base), 0, 16, None)
+    assert rc == -8

@@ -441,3 +441,44 @@ def test_smoothed_bf16_statistics_edge_values(shard):
     torch.cuda.synchronize()
     P.assert_loss_rows(lr, ref, "table edges")
     P.assert_grad_close(g, ref["grad"], "table edges grad")
+
+
+@pytest.mark.parametrize("T,V,dt,eps", [
+    (300, 128256, torch.bfloat16, 0.0),    # two rows per CU, row split register/LDS
+    (96, 32000, torch.bfloat16, 0.1),      # register-resident with smoothing
+    (64, 1000, torch.float32, 0.0),        # fp32, register-resident
+    (40, 128256, torch.bfloat16, 0.1),     # split-V grid (streaming kernels)
+])
+def test_in_place_gradient_matches_out_of_place(T, V, dt, eps):
+    """grad == logits: the gradient overwrites the logits (same pointer,
+    stride and dtype) and equals the out-of-place result bit for bit."""
+    c, logits, target = _case(S.PAGE, T, V, 151 + T, eps=eps, dtype=dt)
+    _say(f"[in place] T={T} V={V} {dt} eps={eps}")
+    ref = vce.fused_fwd_bwd(logits, target, label_smoothing=eps)
+    buf = logits.clone()
+    out = vce.fused_fwd_bwd(buf, target, label_smoothing=eps, grad=buf)
+    torch.cuda.synchronize()
+    assert out["grad"].data_ptr() == buf.data_ptr()
+    assert torch.equal(out["loss_rows"], ref["loss_rows"])
+    assert torch.equal(out["loss"], ref["loss"])
+    assert torch.equal(buf.view(torch.int16 if dt == torch.bfloat16 else torch.int32),
+                       ref["grad"].view(torch.int16 if dt == torch.bfloat16 else torch.int32))
+
+
+def test_in_place_backward_on_shards():
+    """Per-shard backward written over each shard's own logits."""
+    c, logits, target = _case(S.PAGE, 200, 128256, 163, eps=0.1)
+    V, cut = 128256, 64128
+    stats = [vce.forward(logits[:, a:b], target, vocab_start=a, V_total=V,
+                         label_smoothing=0.1)["stats"] for a, b in ((0, cut), (cut, V))]
+    m = vce.merge_shard_stats(stats, target, V, label_smoothing=0.1)
+    ref = [vce.backward(logits[:, a:b], target, m["fin"], m["n_valid"], vocab_start=a,
+                        V_total=V, label_smoothing=0.1) for a, b in ((0, cut), (cut, V))]
+    buf = logits.clone()
+    for a, b in ((0, cut), (cut, V)):
+        view = buf[:, a:b]
+        vce.backward(view, target, m["fin"], m["n_valid"], vocab_start=a, V_total=V,
+                     label_smoothing=0.1, grad=view)
+    torch.cuda.synchronize()
+    assert torch.equal(buf[:, :cut].view(torch.int16), ref[0].view(torch.int16))
+    assert torch.equal(buf[:, cut:].view(torch.int16), ref[1].view(torch.int16))

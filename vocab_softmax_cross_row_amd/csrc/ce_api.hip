@@ -84,6 +84,15 @@ bool vec_ok(const void *logits, int64_t ld, int in_dt, const void *grad, int64_t
     return aligned(grad, ldg * (int64_t)elem_size(out_dt), a);
 }
 
+// The gradient overwrites the logits in place: same address, stride and
+// dtype.  Every kernel reads an element before it writes that element's
+// gradient (a row is read whole before its gradient is written), and no
+// element is read by one thread and written by another.
+bool in_place(const void *logits, int64_t ld, int in_dt, const void *grad, int64_t ldg,
+              int out_dt) {
+    return logits == grad && ld == ldg && in_dt == out_dt;
+}
+
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
     const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
     return x < y + nb && y < x + na;
@@ -355,7 +364,8 @@ int ce_backward(const ce_problem *prob, const void *logits, int logits_dtype,
     if (p.T == 0) return CE_OK;
     if (!logits || !target || !fin || !grad) return CE_ERR_NULL;
     if (p.reduction == CE_RED_MEAN && !n_valid) return CE_ERR_NULL;
-    if (overlaps(logits, matrix_bytes(p.T, p.V_local, p.ld, elem_size(logits_dtype)), grad,
+    if (!in_place(logits, p.ld, logits_dtype, grad, ldg, grad_dtype) &&
+        overlaps(logits, matrix_bytes(p.T, p.V_local, p.ld, elem_size(logits_dtype)), grad,
                  matrix_bytes(p.T, p.V_local, ldg, elem_size(grad_dtype))))
         return CE_ERR_ALIAS;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -395,7 +405,7 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
     if (p.T > 0 && (!logits || !target || !grad)) return CE_ERR_NULL;
     Layout l;
     if ((rc = check_ws(prob, CE_OP_FUSED, ws, ws_bytes, &l)) != CE_OK) return rc;
-    if (p.T > 0 &&
+    if (p.T > 0 && !in_place(logits, p.ld, logits_dtype, grad, ldg, grad_dtype) &&
         overlaps(logits, matrix_bytes(p.T, p.V_local, p.ld, elem_size(logits_dtype)), grad,
                  matrix_bytes(p.T, p.V_local, ldg, elem_size(grad_dtype))))
         return CE_ERR_ALIAS;
@@ -626,7 +636,7 @@ const char *ce_status_str(int status) {
     case CE_ERR_REDUCTION: return "CE_ERR_REDUCTION: unknown reduction";
     case CE_ERR_WORKSPACE: return "CE_ERR_WORKSPACE: workspace missing, misaligned or too small";
     case CE_ERR_SHARDS: return "CE_ERR_SHARDS: n_shards out of range";
-    case CE_ERR_ALIAS: return "CE_ERR_ALIAS: grad overlaps logits";
+    case CE_ERR_ALIAS: return "CE_ERR_ALIAS: grad overlaps logits other than exactly in place";
     case CE_ERR_HIP: return "CE_ERR_HIP: a HIP launch failed";
     case CE_ERR_ARG: return "CE_ERR_ARG: output requested that this call cannot produce";
     default: return "unknown ce_status";
