@@ -361,8 +361,10 @@ def test_api_errors_raise():
     target = torch.zeros(4, dtype=torch.int64, device=DEV)
     with pytest.raises(vce.CEError):
         vce.fused_fwd_bwd(logits, target, label_smoothing=1.0)
+    # grad overlapping the logits other than exactly (in place is allowed)
+    buf = torch.randn((4, 11), device=DEV)
     with pytest.raises(vce.CEError):
-        vce.fused_fwd_bwd(logits, target, grad=logits)   # grad aliases logits
+        vce.fused_fwd_bwd(buf[:, :10], target, grad=buf[:, 1:])
 
 
 # --------------------------------------------------------------------------
