@@ -8,9 +8,9 @@
 // K-columns (1 KB), block (rb, kb) at byte (rb * Ks/16 + kb) * 1024 where Ks
 // is the stored (padded) K, and inside a block lane L's 16 bytes at L * 16
 // hold row rb*32 + L%32, K-columns kb*16 + 8*(L/32) .. +7 -- exactly the
-// A or B register fragment of that MFMA.  A wave fills one LDS block with
-// one 16-byte-per-lane buffer->LDS load of 1 KB of contiguous memory, and
-// reads one fragment with one conflict-free ds_read_b128.  Padding (rows to
+// A or B register fragment of that MFMA.  A wave loads one block as 1 KB of
+// contiguous memory (one 16-byte load per lane), stores it to LDS unchanged,
+// and reads one fragment with one conflict-free ds_read_b128.  Padding (rows to
 // a multiple of 256, K to a multiple of 64) is zero, so loads need no
 // bounds checks.
 //
@@ -20,6 +20,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "ce_device.h"
 #include "ce_launch.h"
 
@@ -27,7 +29,6 @@ namespace vce {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 
 constexpr int kGT = 256;                 // 4 waves, 2 x 2 over the tile
 constexpr int kTile = 256;               // output tile 256 x 256
@@ -167,21 +168,51 @@ void k_gemm(GemmArgs g) {
     const int nk = (int)(g.K / kBK);
     const int a_kbs = (int)(g.a_ks / 16), b_kbs = (int)(g.b_ks / 16);
 
-    // wave w loads row blocks 2w and 2w+1 (4 K blocks each) of A and of B
-    auto load_stage = [&](int kt, int buf) {
-        char *st = lbase + buf * kStage;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int rbl = 2 * wave + (q >> 2), kbl = q & 3;
-            const int kb = g.a_kb0 + kt * 4 + kbl;
-            const int loff = (rbl * 4 + kbl) * 1024;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t *)(st + loff), 16, lane * 16,
-                                                     (rbl * a_kbs + kb) * 1024, 0, 0);
-            const int kbb = g.b_kb0 + kt * 4 + kbl;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(st + 32768 + loff), 16,
-                                                     lane * 16, (rbl * b_kbs + kbb) * 1024, 0, 0);
-        }
+    // Operand stages go global -> registers -> LDS.  Each lane owns 16 slots
+    // of 16 bytes of a stage: q < 8 are A's, q >= 8 B's; wave w's slots are
+    // row blocks 2w and 2w+1, K blocks 0..3.  While stage kt is multiplied
+    // out of one LDS buffer, K groups 0..2 write the slots (stage kt+1,
+    // loaded one stage earlier) to the other buffer and at once reload them
+    // with stage kt+2, so every load has a whole stage to land.  The stage's
+    // one barrier follows group 2: group 3 then already reads the first
+    // fragments of stage kt+1.  Within a group each MFMA is followed by one
+    // LDS read, or by one slot's write and reload, so the matrix pipe is
+    // never left waiting behind a burst of memory instructions.
+    u32x4 stg[16];
+    auto issue_load = [&](int kt, int q) {
+        const int rbl = 2 * wave + ((q & 7) >> 2), kbl = q & 3;
+        if (q < 8)
+            stg[q] = __builtin_amdgcn_raw_buffer_load_b128(
+                ra, lane * 16, (rbl * a_kbs + g.a_kb0 + kt * 4 + kbl) * 1024, 0);
+        else
+            stg[q] = __builtin_amdgcn_raw_buffer_load_b128(
+                rb, lane * 16, (rbl * b_kbs + g.b_kb0 + kt * 4 + kbl) * 1024, 0);
     };
+    auto write_slot = [&](int buf, int q) {
+        const int rbl = 2 * wave + ((q & 7) >> 2), kbl = q & 3;
+        *reinterpret_cast<u32x4 *>(lbase + buf * kStage + (q >= 8 ? 32768 : 0) +
+                                   (rbl * 4 + kbl) * 1024 + lane * 16) = stg[q];
+    };
+    bf16x8 fa[2][4], fb[2][4];
+    auto read_frags = [&](int buf, int kb, int set) {
+        const char *st = lbase + buf * kStage;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            fa[set][i] = *reinterpret_cast<const bf16x8 *>(
+                st + ((wm * 4 + i) * 4 + kb) * 1024 + lane * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            fb[set][j] = *reinterpret_cast<const bf16x8 *>(
+                st + 32768 + ((wn * 4 + j) * 4 + kb) * 1024 + lane * 16);
+    };
+#pragma unroll
+    for (int q = 0; q < 16; ++q) issue_load(0, q);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) write_slot(0, q);
+    if (nk > 1) {
+#pragma unroll
+        for (int q = 0; q < 16; ++q) issue_load(1, q);
+    }
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -190,42 +221,65 @@ void k_gemm(GemmArgs g) {
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    __syncthreads();
+    read_frags(0, 0, 0);
 
-    load_stage(0, 0);
-    for (int kt = 0; kt < nk; ++kt) {
-        __builtin_amdgcn_s_waitcnt(0x0070); // vmcnt(0) lgkmcnt(0): this stage has landed
-        __syncthreads();                     // ... for every wave; the other buffer is free
-        if (kt + 1 < nk) load_stage(kt + 1, (kt + 1) & 1);
-        const char *st = lbase + (kt & 1) * kStage;
-        // fragments of K block kb+1 are read while the 16 MFMAs of kb run,
-        // so the LDS latency hides behind matrix work (the scheduling
-        // barriers keep the compiler from sinking the reads to their uses)
-        bf16x8 fa[2][4], fb[2][4];
-        auto read_frags = [&](int kb, int set) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                fa[set][i] = *reinterpret_cast<const bf16x8 *>(
-                    st + ((wm * 4 + i) * 4 + kb) * 1024 + lane * 16);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                fb[set][j] = *reinterpret_cast<const bf16x8 *>(
-                    st + 32768 + ((wn * 4 + j) * 4 + kb) * 1024 + lane * 16);
-        };
-        read_frags(0, 0);
+    constexpr int q_lo[4] = {0, 6, 11, 16}; // slots written in K groups 0, 1, 2
+    // MORE1: stage kt+1 exists (write it); MORE2: stage kt+2 exists (load
+    // it); NEXT: read the first fragments of stage kt+1 in group 3.  The
+    // flags are compile-time so the loop body has no branches and the wait
+    // before each slot write stays a constant count of later loads.
+    auto run_stage = [&](int kt, auto MORE1, auto MORE2, auto NEXT) {
+        constexpr bool more1 = decltype(MORE1)::value, more2 = decltype(MORE2)::value;
+        constexpr bool next = decltype(NEXT)::value;
+        const int cb = kt & 1, nb = cb ^ 1;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const int cur = kb & 1;
-            if (kb + 1 < 4) read_frags(kb + 1, cur ^ 1);
             __builtin_amdgcn_sched_barrier(0);
+            const bool rd = kb < 3 || next;
+            if (kb < 3) read_frags(cb, kb + 1, cur ^ 1);
+            else if (next) read_frags(nb, 0, cur ^ 1);
+            const int nq = kb < 3 ? q_lo[kb + 1] - q_lo[kb] : 0;
+            if (kb < 3) {
+#pragma unroll
+                for (int q = q_lo[kb]; q < q_lo[kb + 1]; ++q) {
+                    if constexpr (more1) write_slot(nb, q);
+                    if constexpr (more2) issue_load(kt + 2, q);
+                }
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j],
                                                                          acc[i][j], 0, 0, 0);
+            // issue order: MFMA, read (x8), then MFMA, write, load
+            if (rd) {
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // one MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // one LDS read
+                }
+            }
+#pragma unroll
+            for (int w = 0; w < 6; ++w) {
+                if (w < nq) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (more1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // LDS write
+                    if (more2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // global load
+                }
+            }
             __builtin_amdgcn_sched_barrier(0);
+            if (kb == 2) __syncthreads();
         }
-    }
+    };
+    using Yes = std::true_type;
+    using No = std::false_type;
+    int kt = 0;
+    for (; kt + 2 < nk; ++kt) run_stage(kt, Yes{}, Yes{}, Yes{});
+    if (kt + 1 < nk) run_stage(kt++, Yes{}, No{}, Yes{});
+    run_stage(kt, No{}, No{}, No{});
     __syncthreads(); // every wave is done with the operand stages
 
     // Epilogues work on one row block i (32 rows x 128 columns per wave) at a
