@@ -8,11 +8,11 @@
 // K-columns (1 KB), block (rb, kb) at byte (rb * Ks/16 + kb) * 1024 where Ks
 // is the stored (padded) K, and inside a block lane L's 16 bytes at L * 16
 // hold row rb*32 + L%32, K-columns kb*16 + 8*(L/32) .. +7 -- exactly the
-// A or B register fragment of that MFMA.  A wave loads one block as 1 KB of
-// contiguous memory (one 16-byte load per lane), stores it to LDS unchanged,
-// and reads one fragment with one conflict-free ds_read_b128.  Padding (rows to
-// a multiple of 256, K to a multiple of 64) is zero, so loads need no
-// bounds checks.
+// A or B register fragment of that MFMA.  One 16-byte load per lane moves a
+// block as 1 KB of contiguous memory, straight into operand registers (A) or
+// into LDS unchanged (B), where one conflict-free ds_read_b128 reads it back
+// as a fragment.  Padding (rows to a multiple of 256, K to a multiple of 64)
+// is zero, so loads need no bounds checks.
 //
 // Accumulator layout of v_mfma_f32_32x32x16_bf16 (32 x 32 fp32, 16 values
 // per lane): register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
@@ -30,10 +30,10 @@ namespace vce {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kGT = 256;                 // 4 waves, 2 x 2 over the tile
+constexpr int kGT = 256;                 // 4 waves, each 64 rows x 256 columns of the tile
 constexpr int kTile = 256;               // output tile 256 x 256
 constexpr int kBK = 64;                  // K per LDS stage
-constexpr int kStage = 2 * 8 * 4 * 1024; // A and B: 8 row blocks x 4 K blocks each
+constexpr int kStage = 8 * 4 * 1024;     // one B stage in LDS: 8 row blocks x 4 K blocks
 constexpr int kSuperM = 4, kSuperN = 8;  // 32 tiles one XCD works on together
 
 struct LinRow {
@@ -152,7 +152,6 @@ void k_gemm(GemmArgs g) {
     char *lbase = reinterpret_cast<char *>(lds);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
     int tm, tn;
     if (!tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn)) return;
     const int64_t row0 = (int64_t)tm * kTile, col0 = (int64_t)tn * kTile;
@@ -168,93 +167,103 @@ void k_gemm(GemmArgs g) {
     const int nk = (int)(g.K / kBK);
     const int a_kbs = (int)(g.a_ks / 16), b_kbs = (int)(g.b_ks / 16);
 
-    // Operand stages go global -> registers -> LDS.  Each lane owns 16 slots
-    // of 16 bytes of a stage: q < 8 are A's, q >= 8 B's; wave w's slots are
-    // row blocks 2w and 2w+1, K blocks 0..3.  While stage kt is multiplied
-    // out of one LDS buffer, K groups 0..2 write the slots (stage kt+1,
-    // loaded one stage earlier) to the other buffer and at once reload them
-    // with stage kt+2, so every load has a whole stage to land.  The stage's
-    // one barrier follows group 2: group 3 then already reads the first
+    // Wave w owns rows 64w .. 64w+63 of the tile and all 256 columns
+    // (2 x 8 accumulators of 32 x 32).  Its A fragments are its own: they go
+    // from global memory straight into the MFMA operand registers, each
+    // K block's pair reloaded with the next stage as soon as its MFMAs have
+    // issued, so a load has a whole stage to land.  B is shared by the four
+    // waves: global -> registers -> LDS (two stage buffers).  Each lane owns
+    // 8 B slots of 16 bytes per stage (row blocks 2w and 2w+1, K blocks
+    // 0..3); while stage kt is multiplied out of one buffer, K groups 0..2
+    // write the slots (stage kt+1, loaded one stage earlier) to the other
+    // buffer and at once reload them with stage kt+2.  The stage's one
+    // barrier follows group 2, so group 3 already reads the first B
     // fragments of stage kt+1.  Within a group each MFMA is followed by one
     // LDS read, or by one slot's write and reload, so the matrix pipe is
-    // never left waiting behind a burst of memory instructions.
-    u32x4 stg[16];
-    auto issue_load = [&](int kt, int q) {
-        const int rbl = 2 * wave + ((q & 7) >> 2), kbl = q & 3;
-        if (q < 8)
-            stg[q] = __builtin_amdgcn_raw_buffer_load_b128(
-                ra, lane * 16, (rbl * a_kbs + g.a_kb0 + kt * 4 + kbl) * 1024, 0);
-        else
-            stg[q] = __builtin_amdgcn_raw_buffer_load_b128(
-                rb, lane * 16, (rbl * b_kbs + g.b_kb0 + kt * 4 + kbl) * 1024, 0);
+    // never left behind a burst of memory instructions.  Only B passes
+    // through LDS: half the LDS traffic of a 2 x 2 wave layout, which
+    // matters because a bf16 GEMM on this chip runs at a power-limited
+    // clock, and moved bytes cost power.
+    bf16x8 fa[2][4]; // [row block][K block]
+    auto load_a = [&](int kt, int r, int kb) {
+        fa[r][kb] = __builtin_bit_cast(
+            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                        ra, lane * 16, ((2 * wave + r) * a_kbs + g.a_kb0 + kt * 4 + kb) * 1024, 0));
     };
-    auto write_slot = [&](int buf, int q) {
-        const int rbl = 2 * wave + ((q & 7) >> 2), kbl = q & 3;
-        *reinterpret_cast<u32x4 *>(lbase + buf * kStage + (q >= 8 ? 32768 : 0) +
-                                   (rbl * 4 + kbl) * 1024 + lane * 16) = stg[q];
+    u32x4 stg[8];
+    auto load_b = [&](int kt, int q) {
+        stg[q] = __builtin_amdgcn_raw_buffer_load_b128(
+            rb, lane * 16, ((2 * wave + (q >> 2)) * b_kbs + g.b_kb0 + kt * 4 + (q & 3)) * 1024, 0);
     };
-    bf16x8 fa[2][4], fb[2][4];
-    auto read_frags = [&](int buf, int kb, int set) {
+    auto write_b = [&](int buf, int q) {
+        *reinterpret_cast<u32x4 *>(lbase + buf * kStage + ((2 * wave + (q >> 2)) * 4 + (q & 3)) * 1024 +
+                                   lane * 16) = stg[q];
+    };
+    bf16x8 fb[2][8];
+    auto read_b = [&](int buf, int kb, int set) {
         const char *st = lbase + buf * kStage;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            fa[set][i] = *reinterpret_cast<const bf16x8 *>(
-                st + ((wm * 4 + i) * 4 + kb) * 1024 + lane * 16);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            fb[set][j] = *reinterpret_cast<const bf16x8 *>(
-                st + 32768 + ((wn * 4 + j) * 4 + kb) * 1024 + lane * 16);
+        for (int j = 0; j < 8; ++j)
+            fb[set][j] = *reinterpret_cast<const bf16x8 *>(st + (j * 4 + kb) * 1024 + lane * 16);
     };
 #pragma unroll
-    for (int q = 0; q < 16; ++q) issue_load(0, q);
+    for (int q = 0; q < 8; ++q) load_b(0, q);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) write_slot(0, q);
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) load_a(0, r, kb);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) write_b(0, q);
     if (nk > 1) {
 #pragma unroll
-        for (int q = 0; q < 16; ++q) issue_load(1, q);
+        for (int q = 0; q < 8; ++q) load_b(1, q);
     }
 
-    f32x16 acc[4][4];
+    f32x16 acc[2][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     __syncthreads();
-    read_frags(0, 0, 0);
+    read_b(0, 0, 0);
 
-    constexpr int q_lo[4] = {0, 6, 11, 16}; // slots written in K groups 0, 1, 2
-    // MORE1: stage kt+1 exists (write it); MORE2: stage kt+2 exists (load
-    // it); NEXT: read the first fragments of stage kt+1 in group 3.  The
-    // flags are compile-time so the loop body has no branches and the wait
-    // before each slot write stays a constant count of later loads.
-    auto run_stage = [&](int kt, auto MORE1, auto MORE2, auto NEXT) {
+    constexpr int q_lo[4] = {0, 3, 6, 8}; // B slots written in K groups 0, 1, 2
+    // MORE1: stage kt+1 exists (write its B, load its A, read its first B
+    // fragments in group 3); MORE2: stage kt+2 exists (load its B).  The
+    // flags are compile-time so the loop body has no branches and every
+    // wait before a use stays a constant count of later loads.
+    auto run_stage = [&](int kt, auto MORE1, auto MORE2) {
         constexpr bool more1 = decltype(MORE1)::value, more2 = decltype(MORE2)::value;
-        constexpr bool next = decltype(NEXT)::value;
         const int cb = kt & 1, nb = cb ^ 1;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const int cur = kb & 1;
             __builtin_amdgcn_sched_barrier(0);
-            const bool rd = kb < 3 || next;
-            if (kb < 3) read_frags(cb, kb + 1, cur ^ 1);
-            else if (next) read_frags(nb, 0, cur ^ 1);
+            const bool rd = kb < 3 || more1;
+            if (kb < 3) read_b(cb, kb + 1, cur ^ 1);
+            else if (more1) read_b(nb, 0, cur ^ 1);
             const int nq = kb < 3 ? q_lo[kb + 1] - q_lo[kb] : 0;
             if (kb < 3) {
 #pragma unroll
                 for (int q = q_lo[kb]; q < q_lo[kb + 1]; ++q) {
-                    if constexpr (more1) write_slot(nb, q);
-                    if constexpr (more2) issue_load(kt + 2, q);
+                    if constexpr (more1) write_b(nb, q);
+                    if constexpr (more2) load_b(kt + 2, q);
                 }
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j],
+                for (int j = 0; j < 8; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][kb], fb[cur][j],
                                                                          acc[i][j], 0, 0, 0);
-            // issue order: MFMA, read (x8), then MFMA, write, load
+            if constexpr (more1) {
+                load_a(kt + 1, 0, kb);
+                load_a(kt + 1, 1, kb);
+            }
+            // issue order: MFMA, LDS read (x8); MFMA, LDS write, B load;
+            // MFMA, the two A loads
             if (rd) {
 #pragma unroll
                 for (int r = 0; r < 8; ++r) {
@@ -263,12 +272,16 @@ void k_gemm(GemmArgs g) {
                 }
             }
 #pragma unroll
-            for (int w = 0; w < 6; ++w) {
+            for (int w = 0; w < 3; ++w) {
                 if (w < nq) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     if (more1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // LDS write
                     if (more2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // global load
                 }
+            }
+            if (more1) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
             if (kb == 2) __syncthreads();
@@ -276,27 +289,36 @@ void k_gemm(GemmArgs g) {
     };
     using Yes = std::true_type;
     using No = std::false_type;
-    int kt = 0;
-    for (; kt + 2 < nk; ++kt) run_stage(kt, Yes{}, Yes{}, Yes{});
-    if (kt + 1 < nk) run_stage(kt++, Yes{}, No{}, Yes{});
-    run_stage(kt, No{}, No{}, No{});
+    // The first stage is peeled off so that the loop is entered with its
+    // loads outstanding in the loop's own order, and the waits in the loop
+    // stay the counts the steady state needs.
+    if (nk >= 3) {
+        run_stage(0, Yes{}, Yes{});
+        for (int kt = 1; kt + 2 < nk; ++kt) run_stage(kt, Yes{}, Yes{});
+    }
+    if (nk >= 2) run_stage(nk - 2, Yes{}, No{});
+    run_stage(nk - 1, No{}, No{});
     __syncthreads(); // every wave is done with the operand stages
 
-    // Epilogues work on one row block i (32 rows x 128 columns per wave) at a
-    // time, staged through the wave's own LDS slab so that the row-wise work
-    // and the global accesses are contiguous: lanes 16q..16q+15 then own row
+    // Epilogues work on one block e of 32 rows x 128 columns per wave at a
+    // time: rows 64w + 32 (e/2) .., columns 128 (e%2) .. of the tile, staged
+    // through the wave's own LDS slab so that the row-wise work and the
+    // global accesses are contiguous: lanes 16q..16q+15 then own row
     // 4*it + q of the block and 8 consecutive columns each.
     const int h = lane >> 5, lc = lane & 31;
     constexpr int kPitch = 132; // floats per slab row (keeps 16-byte reads spread over banks)
     float *slab = reinterpret_cast<float *>(lbase) + wave * 32 * kPitch;
     const int sub = lane >> 4, c8 = (lane & 15) * 8; // row-pass lane role
-    auto stage = [&](int i) {
+    auto stage = [&](int e) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                slab[(8 * (r >> 2) + 4 * h + (r & 3)) * kPitch + j * 32 + lc] = acc[i][j][r];
+                slab[(8 * (r >> 2) + 4 * h + (r & 3)) * kPitch + j * 32 + lc] =
+                    acc[e >> 1][4 * (e & 1) + j][r];
     };
+    auto blk_row = [&](int e) { return wave * 64 + (e >> 1) * 32; }; // first tile row of block e
+    auto blk_col = [&](int e) { return (e & 1) * 128; };            // first tile column
 
     if constexpr (EPI == GEMM_STATS) {
         // per row of the tile: max and sum of exp over this tile's columns
@@ -320,15 +342,15 @@ void k_gemm(GemmArgs g) {
             own[tid] = 0;
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int e = 0; e < 4; ++e) {
             __syncthreads();
-            stage(i);
+            stage(e);
             __syncthreads();
 #pragma unroll 2
             for (int it = 0; it < 8; ++it) {
                 const int rl = 4 * it + sub;                      // row in the block
-                const int row = wm * 128 + i * 32 + rl;           // row in the tile
-                const int cb = wn * 128 + c8;                     // first column in the tile
+                const int row = blk_row(e) + rl;                  // row in the tile
+                const int cb = blk_col(e) + c8;                   // first column in the tile
                 const float *src = slab + rl * kPitch + c8;
                 const u32x4 p0 = *reinterpret_cast<const u32x4 *>(src);
                 const u32x4 p1 = *reinterpret_cast<const u32x4 *>(src + 4);
@@ -366,9 +388,9 @@ void k_gemm(GemmArgs g) {
                     for (int o = 8; o > 0; o >>= 1) sz += __shfl_xor(sz, o, 64);
                 }
                 if ((lane & 15) == 0) {
-                    pm[wn * 256 + row] = mx;
-                    ps[wn * 256 + row] = s;
-                    pz[wn * 256 + row] = sz;
+                    pm[(e & 1) * 256 + row] = mx;
+                    ps[(e & 1) * 256 + row] = s;
+                    pz[(e & 1) * 256 + row] = sz;
                 }
             }
         }
@@ -417,19 +439,19 @@ void k_gemm(GemmArgs g) {
         char *GT = reinterpret_cast<char *>(g.GT);
         char *G = reinterpret_cast<char *>(g.G);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int e = 0; e < 4; ++e) {
             __syncthreads();
-            stage(i);
+            stage(e);
             __syncthreads();
 #pragma unroll 2
             for (int it = 0; it < 8; ++it) {
                 const int rl = 4 * it + sub;
-                const int64_t n = row0 + wm * 128 + i * 32 + rl;
-                const int64_t v0 = col0 + wn * 128 + c8;
+                const int64_t n = row0 + blk_row(e) + rl;
+                const int64_t v0 = col0 + blk_col(e) + c8;
                 const float *src = slab + rl * kPitch + c8;
                 const u32x4 p0 = *reinterpret_cast<const u32x4 *>(src);
                 const u32x4 p1 = *reinterpret_cast<const u32x4 *>(src + 4);
-                const LinRow R = rc[wm * 128 + i * 32 + rl];
+                const LinRow R = rc[blk_row(e) + rl];
                 const int64_t tcl = (int64_t)R.t - g.col_base;
                 float gv[8];
 #pragma unroll
@@ -460,8 +482,8 @@ void k_gemm(GemmArgs g) {
                 for (int e = 0; e < 4; ++e)
                     w[e] = (uint32_t)bslab[(8 * tau + 2 * e) * kBPitch + c] |
                            ((uint32_t)bslab[(8 * tau + 2 * e + 1) * kBPitch + c] << 16);
-                const int64_t v = col0 + wn * 128 + c;
-                const int64_t n0 = row0 + wm * 128 + i * 32 + 8 * tau;
+                const int64_t v = col0 + blk_col(e) + c;
+                const int64_t n0 = row0 + blk_row(e) + 8 * tau;
                 const int64_t off = frag_off(v >> 5, n0 >> 4, g.ldgt) +
                                     (int64_t)((v & 31) + 32 * ((n0 & 15) >> 3)) * 16;
                 *reinterpret_cast<u32x4 *>(GT + off) = w;
@@ -471,15 +493,15 @@ void k_gemm(GemmArgs g) {
         // plain fp32 result: store, add, or add with Kahan compensation;
         // lanes write 16 bytes, a row's 128 columns are 512 contiguous bytes
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int e = 0; e < 4; ++e) {
             __syncthreads();
-            stage(i);
+            stage(e);
             __syncthreads();
 #pragma unroll 2
             for (int it = 0; it < 8; ++it) {
                 const int rl = 4 * it + sub;
-                const int64_t row = row0 + wm * 128 + i * 32 + rl;
-                const int64_t col = col0 + wn * 128 + c8;
+                const int64_t row = row0 + blk_row(e) + rl;
+                const int64_t col = col0 + blk_col(e) + c8;
                 if (row >= g.M || col >= g.N) continue;
                 const float *src = slab + rl * kPitch + c8;
 #pragma unroll
