@@ -272,29 +272,37 @@ __global__ __launch_bounds__(THREADS) void k_stats(StatsArgs a) {
 // math library) make a 50 KB table in LDS.  The row sum is taken unshifted,
 // sum_j e^{z_j} (fp64 spans e^{-512} .. e^{512}), and scaled by e^{-m} at
 // the end: one LDS read and one fp64 add per element instead of an fp64
-// exponential.  The target and -inf logits read the table's zero entry.
-// |z| < 2^-16 takes e^z = 1 + z + z^2/2 (error below 1e-15); a chunk with
-// |z| >= 512, +inf or NaN is recomputed with the online form.
+// exponential.  The target and -inf logits count zero, |z| < 2^-16 takes
+// e^z = 1 + z + z^2/2 (error below 1e-15), and a chunk with |z| >= 512, +inf
+// or NaN is recomputed with the online form.  The table's lower end keeps
+// the element-by-element path rare: below 2^-16 it is a few logits in a
+// million, and a wave pays for that path whenever one of its lanes needs it.
 
+// Entry 2 off + sign holds e^z of the pattern (kExpTabLo + off) | sign << 15,
+// off < kExpTabHalf; the last two entries (off = kExpTabHalf) are zero.
 __global__ __launch_bounds__(256) void k_exp_table(double *tab) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= kExpTabN) return;
-    if (i == kExpTabZero) {
+    const uint32_t off = (uint32_t)i >> 1, sign = (uint32_t)i & 1u;
+    if (off >= (uint32_t)kExpTabHalf) {
         tab[i] = 0.0;
         return;
     }
-    const uint32_t b = (kExpTabLo + (uint32_t)(i % kExpTabHalf)) | (i >= kExpTabHalf ? 0x8000u : 0u);
+    const uint32_t b = (kExpTabLo + off) | (sign << 15);
     tab[i] = exp((double)__uint_as_float(b << 16));
 }
 
-template <int THREADS, int UNROLL>
-__global__ __launch_bounds__(THREADS) void k_stats_tab(StatsArgs a, const double *tab_g) {
-    using Ch = Chunk<CE_BF16, 8>;
-    __shared__ BlockRed<THREADS> red;
-    __shared__ double tab[kExpTabN];
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef int16_t s16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// One (row, column chunk) unit of the smoothed bf16 statistics, with the
+// table already in LDS.
+template <int THREADS, int UNROLL>
+__device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit, const double *tab,
+                                               BlockRed<THREADS> &red) {
+    using Ch = Chunk<CE_BF16, 8>;
     const int tid = threadIdx.x;
-    const int64_t unit = xcd_major(blockIdx.x, gridDim.x);
     const int64_t row = unit / a.nchunks;
     const int ch = (int)(unit % a.nchunks);
     const int64_t c0 = (int64_t)ch * a.chunk_cols;
@@ -315,21 +323,19 @@ __global__ __launch_bounds__(THREADS) void k_stats_tab(StatsArgs a, const double
         }
         return;
     }
-    for (int i = tid; i < kExpTabN; i += THREADS) tab[i] = tab_g[i];
     const int64_t tl = t - a.vocab_start;
     const int64_t tc = (tl >= c0 && tl < c1) ? tl : -1;
     const char *zrow = static_cast<const char *>(a.logits) + row * a.ld * 2;
     const int64_t nv = (c1 - c0) / 8;
     const int64_t tail0 = c0 + nv * 8;
-    __syncthreads();
 
     // table index of one bf16 pattern; sets *rare when it is outside the table
-    // (the zero entry is read then, and the rare path below corrects it)
+    // (a zero entry is read then, and the rare path below corrects it)
     auto index = [&](uint32_t b, bool &rare) {
         const uint32_t off = (b & 0x7fffu) - kExpTabLo;
         const bool in = off < (uint32_t)kExpTabHalf;
         rare |= !in;
-        return in ? (int)(off + (b >> 15) * kExpTabHalf) : kExpTabZero;
+        return in ? (int)(2 * off + (b >> 15)) : kExpTabZero;
     };
     // the exact term of a pattern outside the table, and whether the online
     // form is needed instead
@@ -348,46 +354,62 @@ __global__ __launch_bounds__(THREADS) void k_stats_tab(StatsArgs a, const double
     double s = 0.0, sz = 0.0;
     float mx = ninf();
     bool redo = false;
-    // One vector of 8 logits.  The common path adds the table entries of all
-    // 8 and takes their max; a vector with a pattern outside the table, or
-    // holding the target, is redone element by element (the target left out).
-    auto vec = [&](const Ch &v, int64_t col) {
-        float zf[8];
+    // the vector (of this chunk's full vectors) that holds the target, or -1
+    const int64_t tvec = tc >= 0 && tc < tail0 ? (tc - c0) / 8 : -1;
+    const char *tabc = reinterpret_cast<const char *>(tab);
+    // One vector of 8 logits, branch-free, so that a group's vectors keep all
+    // their table reads in flight together.  Two logits are handled at a
+    // time in the 16-bit lanes of a word:
+    // - table byte offset: off = |pattern| - kExpTabLo (wrapping below),
+    //   clamped to kExpTabHalf (the zero entries), times 16, plus 8 for a
+    //   negative logit;
+    // - max: the pattern as a signed 16-bit key, ordered as the values are
+    //   (the magnitude bits of a negative pattern flipped);
+    // - the sum of the logits: a bf16 dot product with (1, 1) into fp32.
+    // It returns whether the vector must be redone element by element: an
+    // offset out of range, or the target inside.
+    auto vec_common = [&](const Ch &v, int64_t vi, double &sv, s16x2 &kmax, float &zsum) {
+        u16x2 omax = {0, 0};
+        double t[8];
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        float zs = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) zf[e] = v.get(e);
-        float p[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) p[e] = zf[e];
-#pragma unroll
-        for (int hh = 4; hh > 0; hh >>= 1)
-#pragma unroll
-            for (int e = 0; e < hh; ++e) p[e] += p[e + hh];
-        sz += (double)p[0];
-        bool rare = tc >= col && tc < col + 8;
-        double sv = 0.0;
-        float vm = zf[0];
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t w = v.v[q];
+            const u16x2 off = __builtin_bit_cast(u16x2, w & 0x7fff7fffu) - (u16x2)(uint16_t)kExpTabLo;
+            omax = __builtin_elementwise_max(omax, off);
+            const u16x2 c = __builtin_elementwise_min(off, (u16x2)(uint16_t)kExpTabHalf);
+            const uint32_t a2 = __builtin_bit_cast(uint32_t, c << (uint16_t)4) | ((w >> 12) & 0x00080008u);
+            t[2 * q] = *reinterpret_cast<const double *>(tabc + (a2 & 0xffffu));
+            t[2 * q + 1] = *reinterpret_cast<const double *>(tabc + (a2 >> 16));
+            const s16x2 k = __builtin_bit_cast(s16x2, w);
+            kmax = __builtin_elementwise_max(kmax, k ^ ((k >> (int16_t)15) & (s16x2)(int16_t)0x7fff));
+            zs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, zs, false);
+        }
+        zsum = zs;
+        sv = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+        return vi == tvec || omax.x >= (uint16_t)kExpTabHalf || omax.y >= (uint16_t)kExpTabHalf;
+    };
+    // the float value of a max key
+    auto key_value = [](int16_t k) {
+        const uint32_t b = (uint16_t)(k < 0 ? k ^ 0x7fff : k);
+        return __uint_as_float(b << 16);
+    };
+    // the element-by-element form of a vector (the target left out)
+    auto vec_redo = [&](const Ch &v, int64_t vi, double &sv, float &vm) {
+        const int64_t col = c0 + vi * 8;
+        sv = 0.0;
+        vm = ninf();
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            if (e) vm = fmaxf(vm, zf[e]);
+            if (col + e == tc) continue;
             const uint32_t w = v.v[e >> 1];
-            sv += tab[index((e & 1) ? (w >> 16) : (w & 0xffffu), rare)];
+            const uint32_t b = (e & 1) ? (w >> 16) : (w & 0xffffu);
+            bool r2 = false;
+            const double tv = tab[index(b, r2)];
+            sv += r2 ? rare_term(b, redo) : tv;
+            vm = fmaxf(vm, v.get(e));
         }
-        if (__builtin_expect(rare, 0)) {
-            sv = 0.0;
-            vm = ninf();
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if (col + e == tc) continue;
-                const uint32_t w = v.v[e >> 1];
-                const uint32_t b = (e & 1) ? (w >> 16) : (w & 0xffffu);
-                bool r2 = false;
-                const double tv = tab[index(b, r2)];
-                sv += r2 ? rare_term(b, redo) : tv;
-                vm = fmaxf(vm, zf[e]);
-            }
-        }
-        s += sv;
-        mx = fmaxf(mx, vm);
     };
     const int64_t step = (int64_t)UNROLL * THREADS;
     const int64_t nfull = nv / step * step; // vectors covered by whole iterations
@@ -399,8 +421,36 @@ __global__ __launch_bounds__(THREADS) void k_stats_tab(StatsArgs a, const double
             v[u].load(zrow + (c0 + (base + (int64_t)u * THREADS + tid) * 8) * 2);
     };
     auto work_group = [&](Ch *v, int64_t base) {
+        double sv[UNROLL];
+        float zs[UNROLL];
+        s16x2 km = {(int16_t)-32768, (int16_t)-32768};
+        bool rare[UNROLL], any = false;
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) vec(v[u], c0 + (base + (int64_t)u * THREADS + tid) * 8);
+        for (int u = 0; u < UNROLL; ++u) {
+            rare[u] = vec_common(v[u], base + (int64_t)u * THREADS + tid, sv[u], km, zs[u]);
+            any |= rare[u];
+        }
+        float vm = key_value(km.x > km.y ? km.x : km.y);
+        if (__builtin_expect(any, 0)) {
+            // the group's max again, from the vectors' own element maxima
+            vm = ninf();
+#pragma unroll
+            for (int u = 0; u < UNROLL; ++u) {
+                float m;
+                if (rare[u]) {
+                    vec_redo(v[u], base + (int64_t)u * THREADS + tid, sv[u], m);
+                } else {
+                    m = v[u].get(0);
+#pragma unroll
+                    for (int e = 1; e < 8; ++e) m = fmaxf(m, v[u].get(e));
+                }
+                vm = fmaxf(vm, m);
+            }
+        }
+        static_assert(UNROLL == 4, "the group sums below are written for 4 vectors");
+        s += (sv[0] + sv[1]) + (sv[2] + sv[3]);
+        sz += (double)((zs[0] + zs[1]) + (zs[2] + zs[3]));
+        mx = fmaxf(mx, vm);
     };
     if (nfull > 0) load_group(va, 0);
     for (int64_t base = 0; base < nfull; base += 2 * step) {
@@ -414,7 +464,17 @@ __global__ __launch_bounds__(THREADS) void k_stats_tab(StatsArgs a, const double
     for (int64_t vi = nfull + tid; vi < nv; vi += THREADS) {
         Ch v;
         v.load(zrow + (c0 + vi * 8) * 2);
-        vec(v, c0 + vi * 8);
+        double sv;
+        float zs;
+        s16x2 km = {(int16_t)-32768, (int16_t)-32768};
+        float vm;
+        if (vec_common(v, vi, sv, km, zs))
+            vec_redo(v, vi, sv, vm);
+        else
+            vm = key_value(km.x > km.y ? km.x : km.y);
+        s += sv;
+        sz += (double)zs;
+        mx = fmaxf(mx, vm);
     }
     // scalar tail of the chunk
     for (int64_t col = tail0 + tid; col < c1; col += THREADS) {
@@ -459,6 +519,22 @@ __global__ __launch_bounds__(THREADS) void k_stats_tab(StatsArgs a, const double
         r.s = ms.s;
         r.sz = sz;
         *o = r;
+    }
+}
+
+// Persistent: each workgroup copies the table into LDS once and then walks
+// units blockIdx.x, + gridDim.x, ...; the grid is sized to the workgroups
+// the device holds at once.
+template <int THREADS, int UNROLL>
+__global__ __launch_bounds__(THREADS) void k_stats_tab(StatsArgs a, const double *tab_g) {
+    __shared__ BlockRed<THREADS> red;
+    __shared__ double tab[kExpTabN];
+    for (int i = threadIdx.x; i < kExpTabN; i += THREADS) tab[i] = tab_g[i];
+    __syncthreads();
+    const int64_t units = a.T * a.nchunks;
+    for (int64_t unit = blockIdx.x; unit < units; unit += gridDim.x) {
+        stats_tab_unit<THREADS, UNROLL>(a, unit, tab, red);
+        __syncthreads(); // the unit's reductions are read before `red` is reused
     }
 }
 
@@ -636,8 +712,20 @@ hipError_t launch_stats(const StatsArgs &a, int in_dt, bool vec, hipStream_t str
     const dim3 grid((unsigned)(a.T * a.nchunks));
     const bool ls = a.smoothing != 0;
     if (ls && vec && in_dt == CE_BF16 && a.exp_tab) {
-        hipLaunchKernelGGL((k_stats_tab<kStreamThreads, kStreamUnroll>), grid,
-                           dim3(kStreamThreads), 0, stream, a, a.exp_tab);
+        // as many workgroups as the device holds at once, with the units
+        // spread evenly over them
+        auto kern = k_stats_tab<kStreamThreads, kStreamUnroll>;
+        int dev = 0, cus = 0, per_cu = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess)
+            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)kern, kStreamThreads, 0);
+        if (e != hipSuccess) return e;
+        const int64_t units = a.T * a.nchunks;
+        const int64_t slots = std::max<int64_t>(1, (int64_t)cus * std::max(per_cu, 1));
+        const int64_t per_wg = (units + slots - 1) / slots;
+        const int64_t wgs = (units + per_wg - 1) / per_wg;
+        hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kStreamThreads), 0, stream, a, a.exp_tab);
         return hipGetLastError();
     }
     if (in_dt == CE_BF16)

@@ -40,12 +40,14 @@ struct StatsArgs {
     const double *exp_tab; // smoothing, bf16 rows: e^z per bf16 pattern (kExpTabN), or NULL
 };
 
-// Table of e^z for the bf16 patterns with 2^-16 <= |z| < 2^9 (both signs),
-// plus one zero entry, used by the smoothed statistics of bf16 rows.
+// Table of e^z for the bf16 patterns with 2^-16 <= |z| < 2^9, used by the
+// smoothed statistics of bf16 rows.  Entry 2 off + sign holds the pattern
+// (kExpTabLo + off) | sign << 15, off < kExpTabHalf; the two entries after
+// them (off = kExpTabHalf) are zero.
 constexpr uint32_t kExpTabLo = 0x3780; // bf16 bits of 2^-16
-constexpr int kExpTabHalf = 3200;      // patterns per sign up to 2^9
+constexpr int kExpTabHalf = 3200;      // magnitudes up to 2^9
 constexpr int kExpTabZero = 2 * kExpTabHalf;
-constexpr int kExpTabN = 2 * kExpTabHalf + 1;
+constexpr int kExpTabN = 2 * kExpTabHalf + 2;
 
 struct MergeArgs {
     const ce_row_stats *in; // [S][T]
