@@ -445,6 +445,38 @@ def test_smoothed_bf16_statistics_edge_values(shard):
     P.assert_grad_close(g, ref["grad"], "table edges grad")
 
 
+@pytest.mark.parametrize("eps", [0.1, 0.6])
+def test_smoothed_gradient_where_p_meets_eps_over_v(eps):
+    """With smoothing, a non-target gradient is k (p_j - eps/V), which cancels
+    where p_j is close to eps/V.  Each row holds 4096 zeros and a sweep of
+    2048 logits through [-3, 1] (shifted a little per row), so that p_j
+    passes eps/V in bf16 steps: some entries fall inside the window where the
+    difference is rebuilt from log2(p/u) (|log2(p/u)| < 2^-6), many just
+    outside it, where the plain form must already be within a bf16 ulp."""
+    T, V = 8, 6144
+    z = torch.zeros(T, V)
+    sweep = torch.linspace(-3.0, 1.0, 2048)
+    for r in range(T):
+        z[r, 4096:] = sweep + r * 2.0 ** -9
+    logits = z.to(torch.bfloat16).to(DEV)
+    target = torch.tensor([17 * (r + 1) for r in range(T)], dtype=torch.int64, device=DEV)
+    zz = logits.double().cpu().numpy()
+    lse = np.log(np.exp(zz).sum(axis=1, keepdims=True))
+    w = (zz - lse - math.log(np.float32(eps) / V)) / math.log(2.0)
+    inside = int((np.abs(w) < 2.0 ** -6).sum())
+    near = int(((np.abs(w) >= 2.0 ** -6) & (np.abs(w) < 0.5)).sum())
+    _say(f"[p ~ eps/V] eps={eps}: {inside} entries inside the window, {near} within 0.5")
+    assert inside >= 8 and near >= 400
+    ref = P.oracle_for(logits, target, eps=eps)
+    out = vce.fused_fwd_bwd(logits, target, label_smoothing=eps)
+    f = vce.forward(logits, target, label_smoothing=eps)
+    g = vce.backward(logits, target, f["fin"], f["n_valid"], label_smoothing=eps)
+    torch.cuda.synchronize()
+    P.assert_loss_rows(out["loss_rows"], ref, "p ~ eps/V fused")
+    P.assert_grad_close(out["grad"], ref["grad"], "p ~ eps/V fused grad")
+    P.assert_grad_close(g, ref["grad"], "p ~ eps/V streaming grad")
+
+
 @pytest.mark.parametrize("T,V,dt,eps", [
     (300, 128256, torch.bfloat16, 0.0),    # two rows per CU, row split register/LDS
     (96, 32000, torch.bfloat16, 0.1),      # register-resident with smoothing

@@ -459,10 +459,14 @@ __device__ __forceinline__ double row_scale(int reduction, const float *grad_out
 //   exact (fp32 out, or eps > 0): log2 p = (z kL2E - ch) - cl with C = ch + cl,
 //         accurate near p = 1; the exponential is range-extended so that
 //         subnormal results survive.
-//   eps > 0: g = k p - k u (u = eps / V); where p is within a factor
-//         sqrt(2) of u the difference is rebuilt from w = log2(p / u),
-//         computed with a two-float log2(e) against d2 = d2hi + d2lo, as
-//         k u expm1(w ln 2).
+//   eps > 0: g = k p - k u (u = eps / V).  p carries about 1e-6 relative
+//         error, so k p - k u is off by about 1e-6 p / |p - u| relative,
+//         which passes half a bf16 ulp (2^-9) only for |log2(p/u)| below
+//         about 4e-4.  Where |w| = |log2(p / u)| < 2^-6 (a 40x margin) the
+//         difference is rebuilt from w, computed with a two-float log2(e)
+//         against d2 = d2hi + d2lo, as k u expm1(w ln 2).  The window is
+//         kept narrow because a wave runs that branch whenever one of its
+//         lanes needs it.
 //   target: g = gk.
 struct GradConst {
     float cb, scale, ch, cl, k, gk, ku, lu, d2hi, d2lo;
@@ -508,16 +512,11 @@ __device__ __forceinline__ float exp2_full(float x) {
     return low ? y * 0x1p-64f : y;
 }
 
-// expm1(w ln 2) for |w| <= 1/2 (Taylor series of e^y - 1 in y = w ln 2,
-// |y| <= 0.35, through y^9: truncation below 1e-10 relative).
+// expm1(w ln 2) for |w| <= 2^-6 (Taylor series of e^y - 1 in y = w ln 2,
+// |y| <= 0.011, through y^4: truncation below 2e-10 relative).
 __device__ __forceinline__ float expm1_base2_small(float w) {
     const float y = w * 0.693147180559945309f;
-    float p = 1.0f / 362880.0f;
-    p = fmaf(p, y, 1.0f / 40320.0f);
-    p = fmaf(p, y, 1.0f / 5040.0f);
-    p = fmaf(p, y, 1.0f / 720.0f);
-    p = fmaf(p, y, 1.0f / 120.0f);
-    p = fmaf(p, y, 1.0f / 24.0f);
+    float p = 1.0f / 24.0f;
     p = fmaf(p, y, 1.0f / 6.0f);
     p = fmaf(p, y, 0.5f);
     p = fmaf(p, y, 1.0f);
@@ -530,7 +529,7 @@ __device__ __forceinline__ float grad_elem(float z, const GradConst &c) {
     if constexpr (LS) {
         const float l2p = fmaf(z, kL2E, -c.ch) - c.cl;
         float g = fmaf(fast_exp2(l2p), c.k, -c.ku);
-        if (__builtin_expect(fabsf(l2p - c.lu) < 0.5f, 0)) {
+        if (__builtin_expect(fabsf(l2p - c.lu) < 0x1p-6f, 0)) {
             const float w = fmaf(z, kL2E, -c.d2hi) + fmaf(z, kL2E_lo, -c.d2lo);
             g = c.ku * expm1_base2_small(w);
         }
