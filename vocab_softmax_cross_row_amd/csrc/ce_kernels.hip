@@ -418,7 +418,7 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
     auto load_group = [&](Ch *v, int64_t base) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
-            v[u].load(zrow + (c0 + (base + (int64_t)u * THREADS + tid) * 8) * 2);
+            v[u].template load<true>(zrow + (c0 + (base + (int64_t)u * THREADS + tid) * 8) * 2);
     };
     auto work_group = [&](Ch *v, int64_t base) {
         double sv[UNROLL];
@@ -602,7 +602,7 @@ template <int IN, int OUT, int EPV, int THREADS, int UNROLL, bool LS>
 __global__ __launch_bounds__(THREADS) void k_grad(GradArgs a) {
     using In = Elem<IN>;
     using Ch = Chunk<IN, EPV>;
-    using St = Store<OUT, EPV>;
+    using St = Store<OUT, EPV, true>; // nontemporal: the gradient is not read back here
     constexpr int kOutSize = (OUT == CE_BF16) ? 2 : 4;
     __shared__ GradConst gc_sh;
 
@@ -641,7 +641,7 @@ __global__ __launch_bounds__(THREADS) void k_grad(GradArgs a) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int64_t vi = base + (int64_t)u * THREADS + tid;
-            if (vi < nv) v[u].load(zrow + (c0 + vi * EPV) * In::kSize);
+            if (vi < nv) v[u].template load<true>(zrow + (c0 + vi * EPV) * In::kSize);
         }
         const bool t_here = tc >= c0 + base * EPV && tc < c0 + (base + (int64_t)UNROLL * THREADS) * EPV;
 #pragma unroll
