@@ -131,6 +131,25 @@ __global__ __launch_bounds__(256) void k_linear_rowconst(LinRowArgs a) {
 // The GEMM, with its epilogues.
 // ---------------------------------------------------------------------------
 
+// Reductions over each group of 16 lanes (a DPP row), the result in all 16:
+// swap neighbours, swap pairs, mirror within 8, mirror within 16.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));  // quad_perm [1, 0, 3, 2]
+    x = fmaxf(x, dpp_f<0x4E>(x));  // quad_perm [2, 3, 0, 1]
+    x = fmaxf(x, dpp_f<0x141>(x)); // row_half_mirror
+    return fmaxf(x, dpp_f<0x140>(x)); // row_mirror
+}
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f<0xB1>(x);
+    x += dpp_f<0x4E>(x);
+    x += dpp_f<0x141>(x);
+    return x + dpp_f<0x140>(x);
+}
+
 // Tile of workgroup b.  Workgroups go round-robin over the 8 XCDs; the 32
 // consecutive workgroups of one XCD get one 4 x 8 super-tile, so they share
 // its A and B blocks in that XCD's L2.  False for the padding workgroups.
@@ -341,57 +360,63 @@ void k_gemm(GemmArgs g) {
             zt[tid] = 0.0f;
             own[tid] = 0;
         }
+        // one row-pass step: 8 columns of one row per lane, reduced over the
+        // row's 16 lanes; FULL: every column of the tile is inside N
+        auto row_step = [&](int e, int it, auto FULL) {
+            const int rl = 4 * it + sub;                      // row in the block
+            const int row = blk_row(e) + rl;                  // row in the tile
+            const int cb = blk_col(e) + c8;                   // first column in the tile
+            const float *src = slab + rl * kPitch + c8;
+            const u32x4 p0 = *reinterpret_cast<const u32x4 *>(src);
+            const u32x4 p1 = *reinterpret_cast<const u32x4 *>(src + 4);
+            float z[8];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                z[q] = __uint_as_float(p0[q]);
+                z[4 + q] = __uint_as_float(p1[q]);
+            }
+            const int d = t_l[row] - cb; // the target's place among this lane's columns
+            if (__builtin_expect((unsigned)d < 8u, 0)) {
+                float v = z[0];
+#pragma unroll
+                for (int q = 1; q < 8; ++q) v = (q == d) ? z[q] : v;
+                zt[row] = v;
+                own[row] = 1;
+            }
+            float mx = ninf(), sz = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const bool in = decltype(FULL)::value || col0 + cb + q < g.N;
+                if (LS && in) sz += z[q];
+                if (!in || q == d) z[q] = ninf();
+                mx = fmaxf(mx, z[q]);
+            }
+            mx = row16_max(mx);
+            float s = 0.0f;
+            if (mx != ninf()) {
+                const float K = mx * kL2E;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) s += fast_exp2(fmaf(z[q], kL2E, -K));
+            }
+            s = row16_sum(s);
+            if (LS) sz = row16_sum(sz);
+            if ((lane & 15) == 0) {
+                pm[(e & 1) * 256 + row] = mx;
+                ps[(e & 1) * 256 + row] = s;
+                pz[(e & 1) * 256 + row] = sz;
+            }
+        };
+        const bool full = col0 + kTile <= g.N;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             __syncthreads();
             stage(e);
             __syncthreads();
+            if (full) {
 #pragma unroll 2
-            for (int it = 0; it < 8; ++it) {
-                const int rl = 4 * it + sub;                      // row in the block
-                const int row = blk_row(e) + rl;                  // row in the tile
-                const int cb = blk_col(e) + c8;                   // first column in the tile
-                const float *src = slab + rl * kPitch + c8;
-                const u32x4 p0 = *reinterpret_cast<const u32x4 *>(src);
-                const u32x4 p1 = *reinterpret_cast<const u32x4 *>(src + 4);
-                float z[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    z[e] = __uint_as_float(p0[e]);
-                    z[4 + e] = __uint_as_float(p1[e]);
-                }
-                const int tl = t_l[row];
-                float mx = ninf(), sz = 0.0f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const bool in = col0 + cb + e < g.N;
-                    if (LS && in) sz += z[e];
-                    if (cb + e == tl) {
-                        zt[row] = z[e];
-                        own[row] = 1;
-                    }
-                    if (!in || cb + e == tl) z[e] = ninf();
-                    mx = fmaxf(mx, z[e]);
-                }
-#pragma unroll
-                for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-                float s = 0.0f;
-                if (mx != ninf()) {
-                    const float K = mx * kL2E;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) s += fast_exp2(fmaf(z[e], kL2E, -K));
-                }
-#pragma unroll
-                for (int o = 8; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-                if (LS) {
-#pragma unroll
-                    for (int o = 8; o > 0; o >>= 1) sz += __shfl_xor(sz, o, 64);
-                }
-                if ((lane & 15) == 0) {
-                    pm[(e & 1) * 256 + row] = mx;
-                    ps[(e & 1) * 256 + row] = s;
-                    pz[(e & 1) * 256 + row] = sz;
-                }
+                for (int it = 0; it < 8; ++it) row_step(e, it, std::true_type{});
+            } else {
+                for (int it = 0; it < 8; ++it) row_step(e, it, std::false_type{});
             }
         }
         __syncthreads();
@@ -400,8 +425,8 @@ void k_gemm(GemmArgs g) {
             const float m0 = pm[tid], m1 = pm[256 + tid];
             const float M = fmaxf(m0, m1);
             double s = 0.0;
-            if (m0 != ninf()) s += (double)ps[tid] * exp((double)m0 - (double)M);
-            if (m1 != ninf()) s += (double)ps[256 + tid] * exp((double)m1 - (double)M);
+            if (m0 != ninf()) s += (double)ps[tid] * exp_nonpos((double)m0 - (double)M);
+            if (m1 != ninf()) s += (double)ps[256 + tid] * exp_nonpos((double)m1 - (double)M);
             ce_row_stats o;
             o.m = M;
             o.zt = zt[tid];
