@@ -102,6 +102,16 @@ def test_ragged_tail(V, dt):
     _fused_check(c, logits, target, what=f"ragged {dt} V={V}")
 
 
+@pytest.mark.parametrize("eps", [0.0, 0.1])
+def test_rows_too_long_for_registers_bf16(eps):
+    # bf16 rows longer than 131072 columns do not fit the resident kernels:
+    # the fused entry point streams them (column-chunk statistics, on-device
+    # merge, gradient pass)
+    c, logits, target = _case(S.PAGE, 600, 150001, 77, eps=eps)
+    target[3] = 150000
+    _fused_check(c, logits, target, what=f"long rows eps={eps}")
+
+
 @pytest.mark.parametrize("in_dt,out_dt", [("bf16", torch.float32), ("f32", torch.bfloat16)])
 def test_mixed_dtypes(in_dt, out_dt):
     base = S.PAGE if in_dt == "bf16" else S.TINY
