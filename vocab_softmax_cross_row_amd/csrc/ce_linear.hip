@@ -20,6 +20,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "ce_device.h"
@@ -164,15 +165,22 @@ __device__ __forceinline__ bool tile_of(int64_t b, int tiles_m, int tiles_n, int
     return tm < tiles_m && tn < tiles_n;
 }
 
+// Number of tile ids tile_of walks: whole groups of 8 super-tiles (one per
+// XCD), padding included.
+__host__ __device__ __forceinline__ int64_t tile_ids(int tiles_m, int tiles_n) {
+    const int64_t supers = (int64_t)((tiles_m + kSuperM - 1) / kSuperM) * ((tiles_n + kSuperN - 1) / kSuperN);
+    return (supers + kXcds - 1) / kXcds * kXcds * kSuperM * kSuperN;
+}
+
+// One 256 x 256 output tile: main loop and epilogue.
 template <int EPI, bool LS>
-__global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_gemm(GemmArgs g) {
-    extern __shared__ __attribute__((aligned(16))) u32x4 lds[];
-    char *lbase = reinterpret_cast<char *>(lds);
-    const int tid = threadIdx.x, lane = tid & 63;
+__device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, char *lbase) {
+    // opaque per tile: values derived from the thread index are not hoisted
+    // out of the tile loop, where they would stay live through every tile
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int tm, tn;
-    if (!tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn)) return;
     const int64_t row0 = (int64_t)tm * kTile, col0 = (int64_t)tn * kTile;
 
     // the 8 row blocks of A and of B this tile reads, as buffer resources
@@ -317,6 +325,16 @@ void k_gemm(GemmArgs g) {
     }
     if (nk >= 2) run_stage(nk - 2, Yes{}, No{});
     run_stage(nk - 1, No{}, No{});
+    // Every accumulator is pinned here.  MFMAs touch no memory, so a barrier
+    // alone does not keep them above the epilogue: the compiler has sunk the
+    // last ones into the epilogue, among its LDS writes of accumulators, and
+    // a write issued that soon after the MFMA producing its source read a
+    // stale value (the hazard padding inserted for it was too short).
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads(); // every wave is done with the operand stages
 
     // Epilogues work on one block e of 32 rows x 128 columns per wave at a
@@ -570,6 +588,31 @@ void k_gemm(GemmArgs g) {
     }
 }
 
+// Persistent: one workgroup per CU walks tile ids blockIdx.x, + gridDim.x,
+// ...; the grid is a multiple of 8, so a workgroup stays on one XCD and the
+// ids of a round still form one super-tile per XCD.  The G epilogue keeps
+// one tile per workgroup: inside a tile loop it would not fit the registers.
+template <int EPI>
+constexpr bool kGemmPersistent = EPI != GEMM_GRAD;
+
+template <int EPI, bool LS>
+__global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_gemm(GemmArgs g) {
+    extern __shared__ __attribute__((aligned(16))) u32x4 lds[];
+    char *lbase = reinterpret_cast<char *>(lds);
+    int tm, tn;
+    if constexpr (!kGemmPersistent<EPI>) {
+        if (tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn)) gemm_tile<EPI, LS>(g, tm, tn, lbase);
+        return;
+    }
+    const int64_t ids = tile_ids(g.tiles_m, g.tiles_n);
+    for (int64_t b = blockIdx.x; b < ids; b += gridDim.x) {
+        if (!tile_of(b, g.tiles_m, g.tiles_n, tm, tn)) continue;
+        gemm_tile<EPI, LS>(g, tm, tn, lbase);
+        __syncthreads(); // the epilogue's LDS is the next tile's stage buffers
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Merge of the per-tile statistics of each row ([M][S], row-major) and the
 // finalize: one wave per row, shards spread over the lanes, combined by a
@@ -678,10 +721,17 @@ static hipError_t gemm_launch(const GemmArgs &g, hipStream_t stream) {
         if (e != hipSuccess) return e;
         attr = true;
     }
-    const int64_t supers = ((g.tiles_m + kSuperM - 1) / kSuperM) *
-                           ((g.tiles_n + kSuperN - 1) / kSuperN);
-    const int64_t groups = (supers + kXcds - 1) / kXcds;
-    const dim3 grid((unsigned)(groups * kXcds * kSuperM * kSuperN));
+    // as many workgroups as the device holds at once, a multiple of 8
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_gemm<EPI, LS>, kGT,
+                                                         kGemmLdsBytes);
+    if (e != hipSuccess) return e;
+    const int64_t ids = tile_ids(g.tiles_m, g.tiles_n);
+    const int64_t slots = std::max<int64_t>(kXcds, (int64_t)cus * std::max(per_cu, 1) / kXcds * kXcds);
+    const dim3 grid((unsigned)(kGemmPersistent<EPI> ? std::min(ids, slots) : ids));
     hipLaunchKernelGGL((k_gemm<EPI, LS>), grid, dim3(kGT), kGemmLdsBytes, stream, g);
     return hipGetLastError();
 }
