@@ -334,6 +334,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+    // and 32 wait states on top of the compiler's own padding, whatever the
+    // order of the last K group's MFMAs (once per tile)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) asm volatile("s_nop 7");
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads(); // every wave is done with the operand stages
 
