@@ -25,6 +25,11 @@ constexpr int64_t kMaxChunks = 64;
 // kernel when there are fewer rows than this and rows are long.
 constexpr int64_t kResidentMinRows = 512;
 constexpr int64_t kResidentSplitCols = 16384;
+// bf16 rows with label smoothing longer than this go to the streaming path:
+// its statistics read e^z from an LDS table, while the resident kernel
+// takes an fp64 exponential per logit, and from about 64K columns the extra
+// pass costs less than those exponentials (page scale 2.4 against 3.7 ms).
+constexpr int64_t kSmoothedResidentMaxCols = 32768;
 
 constexpr size_t kAlign = 256;
 
@@ -418,7 +423,9 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
     if (p.T > 0) {
         const bool vec = vec_ok(logits, p.ld, logits_dtype, grad, ldg, grad_dtype);
         const bool split = p.T < kResidentMinRows && p.V_local >= kResidentSplitCols;
-        if (vec && !split && resident_threads(logits_dtype, p.V_local) > 0) {
+        const bool smoothed_long = p.label_smoothing > 0.0f && logits_dtype == CE_BF16 &&
+                                   p.V_local > kSmoothedResidentMaxCols;
+        if (vec && !split && !smoothed_long && resident_threads(logits_dtype, p.V_local) > 0) {
             FusedArgs fa;
             fa.logits = logits;
             fa.ld = p.ld;
