@@ -163,6 +163,40 @@ def test_unaligned_rows_take_the_scalar_path():
     P.assert_grad_close(out["grad"], ref["grad"], "unaligned grad")
 
 
+@pytest.mark.parametrize("dt,T,V,eps", [
+    ("bf16", 520, 2001, 0.0),      # odd width: every row starts at a different 16-byte offset
+    ("bf16", 40, 50257, 0.0),      # short T: column chunks, each with its own head
+    ("bf16", 600, 50257, 0.1),     # smoothing: the table statistics peel the head too
+    ("f32", 520, 1001, 0.0),
+])
+def test_odd_width_rows_take_the_vector_path(dt, T, V, eps):
+    """Contiguous rows of odd width are not 16-byte aligned, but a contiguous
+    gradient has the same misalignment in every row: the streaming kernels
+    peel each row's head up to the first 16-byte boundary and use vectors
+    after it.  Fused, in place, and per-shard forward/backward on views that
+    start at an odd column."""
+    base = S.PAGE if dt == "bf16" else S.TINY
+    c, logits, target = _case(base, T, V, 500 + V % 97, eps=eps)
+    _fused_check(c, logits, target, what=f"odd width {dt} T={T} V={V} eps={eps}")
+    ref = P.oracle_for(logits, target, eps=eps)
+    buf = logits.clone()
+    out = vce.fused_fwd_bwd(buf, target, grad=buf, label_smoothing=eps)
+    torch.cuda.synchronize()
+    P.assert_grad_close(out["grad"], ref["grad"], "odd width in place")
+    # shards that start at odd columns of the same rows
+    edges = [0, 3, V // 2 + 1, V]
+    stats = [vce.forward(logits[:, a:b], target, vocab_start=a, V_total=V,
+                         label_smoothing=eps)["stats"] for a, b in zip(edges[:-1], edges[1:])]
+    m = vce.merge_shard_stats(stats, target, V, label_smoothing=eps)
+    g = torch.empty_like(logits)
+    for a, b in zip(edges[:-1], edges[1:]):
+        vce.backward(logits[:, a:b], target, m["fin"], m["n_valid"], grad=g[:, a:b],
+                     vocab_start=a, V_total=V, label_smoothing=eps)
+    torch.cuda.synchronize()
+    P.assert_loss_rows(m["loss_rows"], ref, "odd width shards")
+    P.assert_grad_close(g, ref["grad"], "odd width shard grads")
+
+
 # --------------------------------------------------------------------------
 # unfused path: forward, split-vocabulary shards, merge, backward
 # --------------------------------------------------------------------------

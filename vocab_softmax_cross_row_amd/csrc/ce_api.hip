@@ -89,6 +89,23 @@ bool vec_ok(const void *logits, int64_t ld, int in_dt, const void *grad, int64_t
     return aligned(grad, ldg * (int64_t)elem_size(out_dt), a);
 }
 
+// The streaming kernels' vector path: it starts each row (chunk) at the
+// logits' first 16-byte boundary, so logits rows need only be element
+// aligned; gradient rows must then be aligned for their vector stores at the
+// same columns: already so, or the same element size with the same address
+// residue mod 16 in every row (a contiguous gradient of a contiguous, odd
+// width logits tensor, or the logits themselves).
+bool stream_vec_ok(const void *logits, int64_t ld, int in_dt, const void *grad, int64_t ldg,
+                   int out_dt) {
+    if (vec_ok(logits, ld, in_dt, grad, ldg, out_dt)) return true;
+    const size_t in_size = elem_size(in_dt), out_size = elem_size(out_dt);
+    if (reinterpret_cast<uintptr_t>(logits) % in_size != 0) return false;
+    if (!grad) return true;
+    if (in_size != out_size) return false;
+    const intptr_t d = reinterpret_cast<intptr_t>(grad) - reinterpret_cast<intptr_t>(logits);
+    return d % 16 == 0 && ((ldg - ld) * (int64_t)in_size) % 16 == 0;
+}
+
 // The gradient overwrites the logits in place: same address, stride and
 // dtype.  Every kernel reads an element before it writes that element's
 // gradient (a row is read whole before its gradient is written), and no
@@ -286,7 +303,7 @@ int ce_forward(const ce_problem *prob, const void *logits, int logits_dtype,
     sa.out = pl.nchunks > 1 ? at<ce_row_stats>(ws, l.partial) : stats;
     sa.smoothing = p.label_smoothing > 0.0f;
     sa.exp_tab = nullptr;
-    const bool vec = vec_ok(logits, p.ld, logits_dtype, nullptr, 0, CE_F32);
+    const bool vec = stream_vec_ok(logits, p.ld, logits_dtype, nullptr, 0, CE_F32);
     if (sa.smoothing && vec && logits_dtype == CE_BF16) {
         double *tab = at<double>(ws, l.exp_tab);
         VCE_TRY(launch_exp_table(tab, s));
@@ -392,7 +409,7 @@ int ce_backward(const ce_problem *prob, const void *logits, int logits_dtype,
     ga.ldg = ldg;
     ga.nchunks = pl.nchunks;
     ga.chunk_cols = pl.chunk_cols;
-    const bool vec = vec_ok(logits, p.ld, logits_dtype, grad, ldg, grad_dtype);
+    const bool vec = stream_vec_ok(logits, p.ld, logits_dtype, grad, ldg, grad_dtype);
     VCE_TRY(launch_grad(ga, logits_dtype, grad_dtype, vec, p.T, s));
     return CE_OK;
 }
@@ -422,6 +439,7 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
 
     if (p.T > 0) {
         const bool vec = vec_ok(logits, p.ld, logits_dtype, grad, ldg, grad_dtype);
+        const bool svec = stream_vec_ok(logits, p.ld, logits_dtype, grad, ldg, grad_dtype);
         const bool split = p.T < kResidentMinRows && p.V_local >= kResidentSplitCols;
         const bool smoothed_long = p.label_smoothing > 0.0f && logits_dtype == CE_BF16 &&
                                    p.V_local > kSmoothedResidentMaxCols;
@@ -457,12 +475,12 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
             sa.out = at<ce_row_stats>(ws, l.partial);
             sa.smoothing = p.label_smoothing > 0.0f;
             sa.exp_tab = nullptr;
-            if (sa.smoothing && vec && logits_dtype == CE_BF16) {
+            if (sa.smoothing && svec && logits_dtype == CE_BF16) {
                 double *tab = at<double>(ws, l.exp_tab);
                 VCE_TRY(launch_exp_table(tab, s));
                 sa.exp_tab = tab;
             }
-            VCE_TRY(launch_stats(sa, logits_dtype, vec, s));
+            VCE_TRY(launch_stats(sa, logits_dtype, svec, s));
 
             ce_row_final *fin = at<ce_row_final>(ws, l.fin);
             MergeArgs ma;
@@ -494,7 +512,7 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
             ga.ldg = ldg;
             ga.nchunks = pl.nchunks;
             ga.chunk_cols = pl.chunk_cols;
-            VCE_TRY(launch_grad(ga, logits_dtype, grad_dtype, vec, p.T, s));
+            VCE_TRY(launch_grad(ga, logits_dtype, grad_dtype, svec, p.T, s));
         }
     }
     if (loss && p.reduction != CE_RED_NONE)

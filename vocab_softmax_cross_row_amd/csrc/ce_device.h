@@ -93,6 +93,18 @@ __device__ __forceinline__ void st16(void *p, u32x4 v) {
 // ---------------------------------------------------------------------------
 // A group of EPV consecutive logits of one row, kept in their storage format.
 // ---------------------------------------------------------------------------
+// Elements before the first 16-byte boundary at or after p (at most n), for
+// vector loads of EPV elements of SIZE bytes; 0 for one-element "vectors".
+template <int SIZE, int EPV>
+__device__ __forceinline__ int64_t head_elems(const void *p, int64_t n) {
+    if constexpr (EPV == 1) {
+        return 0;
+    } else {
+        const int64_t h = (int64_t)((16u - (uint32_t)(reinterpret_cast<uintptr_t>(p) & 15u)) & 15u) / SIZE;
+        return h < n ? h : n;
+    }
+}
+
 template <int DT, int EPV>
 struct Chunk;
 

@@ -157,8 +157,11 @@ __device__ __forceinline__ void stats_online(const char *zrow, int64_t c0, int64
     using In = Elem<IN>;
     using Ch = Chunk<IN, EPV>;
     const int tid = threadIdx.x;
-    const int64_t nv = (c1 - c0) / EPV; // full vectors of this chunk
-    const int64_t tail0 = c0 + nv * EPV;
+    // vectors start at the first 16-byte boundary at or after c0; the head
+    // before it (rows that are not 16-byte aligned) joins the scalar tail
+    const int64_t v0 = c0 + head_elems<In::kSize, EPV>(zrow + c0 * In::kSize, c1 - c0);
+    const int64_t nv = (c1 - v0) / EPV; // full vectors of this chunk
+    const int64_t tail0 = v0 + nv * EPV;
     Online<LS> acc;
     double sz = 0.0;
     for (int64_t base = 0; base < nv; base += (int64_t)UNROLL * THREADS) {
@@ -167,18 +170,18 @@ __device__ __forceinline__ void stats_online(const char *zrow, int64_t c0, int64
         for (int u = 0; u < UNROLL; ++u) {
             const int64_t vi = base + (int64_t)u * THREADS + tid;
             if (vi < nv)
-                v[u].load(zrow + (c0 + vi * EPV) * In::kSize);
+                v[u].load(zrow + (v0 + vi * EPV) * In::kSize);
             else
                 v[u].fill_ninf();
         }
         // one rescale per UNROLL vectors: the max of the whole group first;
         // the target test is uniform over the group's column span first
-        const bool t_here = tc >= c0 + base * EPV && tc < c0 + (base + (int64_t)UNROLL * THREADS) * EPV;
+        const bool t_here = tc >= v0 + base * EPV && tc < v0 + (base + (int64_t)UNROLL * THREADS) * EPV;
         float vm = ninf();
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int64_t vi = base + (int64_t)u * THREADS + tid;
-            const int64_t col = c0 + vi * EPV;
+            const int64_t col = v0 + vi * EPV;
             if (LS && vi < nv) {
                 float p[EPV];
 #pragma unroll
@@ -201,8 +204,9 @@ __device__ __forceinline__ void stats_online(const char *zrow, int64_t c0, int64
                 for (int e = 0; e < EPV; ++e) acc.add(acc.term(v[u].get(e)));
         }
     }
-    // scalar tail of the chunk
-    for (int64_t col = tail0 + tid; col < c1; col += THREADS) {
+    // scalar head and tail of the chunk
+    for (int64_t k = tid; k < (v0 - c0) + (c1 - tail0); k += THREADS) {
+        const int64_t col = k < v0 - c0 ? c0 + k : tail0 + (k - (v0 - c0));
         float z = In::load1(zrow + col * In::kSize);
         if (LS) sz += (double)z;
         if (col == tc) z = ninf();
@@ -218,7 +222,6 @@ __device__ __forceinline__ void stats_online(const char *zrow, int64_t c0, int64
 template <int IN, int EPV, int THREADS, int UNROLL, bool LS>
 __global__ __launch_bounds__(THREADS) void k_stats(StatsArgs a) {
     using In = Elem<IN>;
-    using Ch = Chunk<IN, EPV>;
     __shared__ BlockRed<THREADS> red;
 
     const int tid = threadIdx.x;
@@ -326,8 +329,11 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
     const int64_t tl = t - a.vocab_start;
     const int64_t tc = (tl >= c0 && tl < c1) ? tl : -1;
     const char *zrow = static_cast<const char *>(a.logits) + row * a.ld * 2;
-    const int64_t nv = (c1 - c0) / 8;
-    const int64_t tail0 = c0 + nv * 8;
+    // vectors start at the first 16-byte boundary at or after c0; the head
+    // before it joins the scalar tail
+    const int64_t v0 = c0 + head_elems<2, 8>(zrow + c0 * 2, c1 - c0);
+    const int64_t nv = (c1 - v0) / 8;
+    const int64_t tail0 = v0 + nv * 8;
 
     // table index of one bf16 pattern; sets *rare when it is outside the table
     // (a zero entry is read then, and the rare path below corrects it)
@@ -355,7 +361,7 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
     float mx = ninf();
     bool redo = false;
     // the vector (of this chunk's full vectors) that holds the target, or -1
-    const int64_t tvec = tc >= 0 && tc < tail0 ? (tc - c0) / 8 : -1;
+    const int64_t tvec = tc >= v0 && tc < tail0 ? (tc - v0) / 8 : -1;
     const char *tabc = reinterpret_cast<const char *>(tab);
     // One vector of 8 logits, branch-free, so that a group's vectors keep all
     // their table reads in flight together.  Two logits are handled at a
@@ -397,7 +403,7 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
     };
     // the element-by-element form of a vector (the target left out)
     auto vec_redo = [&](const Ch &v, int64_t vi, double &sv, float &vm) {
-        const int64_t col = c0 + vi * 8;
+        const int64_t col = v0 + vi * 8;
         sv = 0.0;
         vm = ninf();
 #pragma unroll
@@ -418,7 +424,7 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
     auto load_group = [&](Ch *v, int64_t base) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u)
-            v[u].template load<true>(zrow + (c0 + (base + (int64_t)u * THREADS + tid) * 8) * 2);
+            v[u].template load<true>(zrow + (v0 + (base + (int64_t)u * THREADS + tid) * 8) * 2);
     };
     auto work_group = [&](Ch *v, int64_t base) {
         double sv[UNROLL];
@@ -463,7 +469,7 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
     }
     for (int64_t vi = nfull + tid; vi < nv; vi += THREADS) {
         Ch v;
-        v.load(zrow + (c0 + vi * 8) * 2);
+        v.load(zrow + (v0 + vi * 8) * 2);
         double sv;
         float zs;
         s16x2 km = {(int16_t)-32768, (int16_t)-32768};
@@ -476,8 +482,9 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
         sz += (double)zs;
         mx = fmaxf(mx, vm);
     }
-    // scalar tail of the chunk
-    for (int64_t col = tail0 + tid; col < c1; col += THREADS) {
+    // scalar head and tail of the chunk
+    for (int64_t k = tid; k < (v0 - c0) + (c1 - tail0); k += THREADS) {
+        const int64_t col = k < v0 - c0 ? c0 + k : tail0 + (k - (v0 - c0));
         const uint32_t b = *reinterpret_cast<const uint16_t *>(zrow + col * 2);
         const float z = __uint_as_float(b << 16);
         sz += (double)z;
@@ -612,19 +619,25 @@ __global__ __launch_bounds__(THREADS) void k_grad(GradArgs a) {
     const int ch = (int)(unit % a.nchunks);
     const int64_t c0 = (int64_t)ch * a.chunk_cols;
     const int64_t c1 = std::min(a.V_local, c0 + a.chunk_cols);
-    const int64_t nv = (c1 - c0) / EPV;
-    const int64_t tail0 = c0 + nv * EPV;
     const char *zrow = static_cast<const char *>(a.logits) + row * a.ld * In::kSize;
     char *grow = static_cast<char *>(a.grad) + row * a.ldg * kOutSize;
+    // vectors start at the first 16-byte boundary of the logits at or after
+    // c0 (the host only takes this kernel when the gradient row is then
+    // aligned for its vector stores too); the head joins the scalar tail
+    const int64_t v0 = c0 + head_elems<In::kSize, EPV>(zrow + c0 * In::kSize, c1 - c0);
+    const int64_t nv = (c1 - v0) / EPV;
+    const int64_t tail0 = v0 + nv * EPV;
+    const int64_t nscalar = (v0 - c0) + (c1 - tail0);
+    auto scalar_col = [&](int64_t k) { return k < v0 - c0 ? c0 + k : tail0 + (k - (v0 - c0)); };
 
     const ce_row_final f = a.fin[row];
     if (f.status != 1) {
         float zero[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) zero[e] = 0.0f;
-        for (int64_t vi = tid; vi < nv; vi += THREADS) St::put(grow + (c0 + vi * EPV) * kOutSize, zero);
-        for (int64_t col = tail0 + tid; col < c1; col += THREADS)
-            Store<OUT, 1>::put(grow + col * kOutSize, zero);
+        for (int64_t vi = tid; vi < nv; vi += THREADS) St::put(grow + (v0 + vi * EPV) * kOutSize, zero);
+        for (int64_t k = tid; k < nscalar; k += THREADS)
+            Store<OUT, 1>::put(grow + scalar_col(k) * kOutSize, zero);
         return;
     }
     if (tid == 0) {
@@ -641,14 +654,14 @@ __global__ __launch_bounds__(THREADS) void k_grad(GradArgs a) {
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int64_t vi = base + (int64_t)u * THREADS + tid;
-            if (vi < nv) v[u].template load<true>(zrow + (c0 + vi * EPV) * In::kSize);
+            if (vi < nv) v[u].template load<true>(zrow + (v0 + vi * EPV) * In::kSize);
         }
-        const bool t_here = tc >= c0 + base * EPV && tc < c0 + (base + (int64_t)UNROLL * THREADS) * EPV;
+        const bool t_here = tc >= v0 + base * EPV && tc < v0 + (base + (int64_t)UNROLL * THREADS) * EPV;
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
             const int64_t vi = base + (int64_t)u * THREADS + tid;
             if (vi >= nv) continue;
-            const int64_t col = c0 + vi * EPV;
+            const int64_t col = v0 + vi * EPV;
             float g[EPV];
 #pragma unroll
             for (int e = 0; e < EPV; ++e) g[e] = grad_elem<OUT, LS>(v[u].get(e), c);
@@ -660,7 +673,8 @@ __global__ __launch_bounds__(THREADS) void k_grad(GradArgs a) {
             St::put(grow + col * kOutSize, g);
         }
     }
-    for (int64_t col = tail0 + tid; col < c1; col += THREADS) {
+    for (int64_t k = tid; k < nscalar; k += THREADS) {
+        const int64_t col = scalar_col(k);
         const float z = In::load1(zrow + col * In::kSize);
         float g;
         g = (col == tc) ? c.gk : grad_elem<OUT, LS>(z, c);
