@@ -165,6 +165,8 @@ def test_unaligned_rows_take_the_scalar_path():
 
 @pytest.mark.parametrize("dt,T,V,eps", [
     ("bf16", 520, 2001, 0.0),      # odd width: every row starts at a different 16-byte offset
+    ("bf16", 520, 2001, 0.1),      # resident with smoothing
+    ("bf16", 520, 100003, 0.0),    # beyond 65536: the resident kernel, not the LDS-split one
     ("bf16", 40, 50257, 0.0),      # short T: column chunks, each with its own head
     ("bf16", 600, 50257, 0.1),     # smoothing: the table statistics peel the head too
     ("f32", 520, 1001, 0.0),

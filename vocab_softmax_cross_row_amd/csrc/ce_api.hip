@@ -443,7 +443,7 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
         const bool split = p.T < kResidentMinRows && p.V_local >= kResidentSplitCols;
         const bool smoothed_long = p.label_smoothing > 0.0f && logits_dtype == CE_BF16 &&
                                    p.V_local > kSmoothedResidentMaxCols;
-        if (vec && !split && !smoothed_long && resident_threads(logits_dtype, p.V_local) > 0) {
+        if (svec && !split && !smoothed_long && resident_threads(logits_dtype, p.V_local) > 0) {
             FusedArgs fa;
             fa.logits = logits;
             fa.ld = p.ld;
@@ -457,7 +457,7 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
             fa.loss_rows = lr;
             fa.reduction = p.reduction;
             fa.eps = p.label_smoothing;
-            VCE_TRY(launch_fused_resident(fa, logits_dtype, grad_dtype, p.T, s));
+            VCE_TRY(launch_fused_resident(fa, logits_dtype, grad_dtype, p.T, vec, s));
         } else {
             // streaming: stats (column chunks) -> merge + finalize -> gradient
             const Plan pl = plan_chunks(p.T, p.V_local);

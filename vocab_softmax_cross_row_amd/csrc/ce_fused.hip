@@ -44,11 +44,20 @@ __global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
     const int tid = threadIdx.x;
     const int64_t row = xcd_major(blockIdx.x, gridDim.x);
     const int V = (int)a.V;
-    const int nvec = V / EPV;
-    const int tail0 = nvec * EPV;
-    const int ntail = V - tail0;
     const char *zrow = static_cast<const char *>(a.logits) + row * a.ld * In::kSize;
     char *grow = static_cast<char *>(a.grad) + row * a.ldg * kOutSize;
+    // Vectors start at the row's first 16-byte boundary (rows of odd width
+    // are not aligned; the host takes this kernel for them only when the
+    // gradient row is then aligned too).  The head before it and the tail
+    // after the last vector are scalar slots, one per thread: slot k is
+    // column k of the head, or column tail0 + (k - head) of the tail.
+    const int head = (int)head_elems<In::kSize, EPV>(zrow, V);
+    const int nvec = (V - head) / EPV;
+    const int tail0 = head + nvec * EPV;
+    const int nscal = head + (V - tail0);
+    const int scol = tid < head ? tid : tail0 + (tid - head); // this thread's scalar slot
+    const char *zvec = zrow + head * In::kSize;
+    char *gvec = grow + head * kOutSize;
 
     const int64_t t64 = a.target[row];
     if (t64 == a.ignore_index || t64 < 0 || t64 >= V) {
@@ -59,9 +68,9 @@ __global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int vi = i * THREADS + tid;
-            if (vi < nvec) St::put(grow + vi * EPV * kOutSize, zero);
+            if (vi < nvec) St::put(gvec + vi * EPV * kOutSize, zero);
         }
-        if (tid < ntail) Store<OUT, 1>::put(grow + (tail0 + tid) * kOutSize, zero);
+        if (tid < nscal) Store<OUT, 1>::put(grow + scol * kOutSize, zero);
         if (tid == 0) a.loss_rows[row] = (t64 == a.ignore_index) ? 0.0f : __builtin_nanf("");
         return;
     }
@@ -73,20 +82,21 @@ __global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
     for (int i = 0; i < NV; ++i) {
         const int vi = i * THREADS + tid;
         if (vi < nvec)
-            v[i].template load<true>(zrow + vi * EPV * In::kSize);
+            v[i].template load<true>(zvec + vi * EPV * In::kSize);
         else
             v[i].fill_ninf();
     }
-    float ztail = ninf();
-    if (tid < ntail) ztail = In::load1(zrow + (tail0 + tid) * In::kSize);
+    float ztail = ninf(); // this thread's scalar slot
+    if (tid < nscal) ztail = In::load1(zrow + scol * In::kSize);
 
     // where the target sits: vector tv = slot t_slot of thread t_thread
     // (wave t_wave), element te; or the scalar tail.  t is the same for the
     // whole workgroup, and readfirstlane makes the slot and wave tests
     // scalar branches, so only the owner wave does any work for it.
-    const int tv = t / EPV;
-    const int te = __builtin_amdgcn_readfirstlane(t - tv * EPV);
-    const bool t_in_vec = t < tail0;
+    const int tv = (t - head) / EPV;
+    const int te = __builtin_amdgcn_readfirstlane((t - head) - tv * EPV);
+    const bool t_in_vec = t >= head && t < tail0;
+    const int t_scal = t < head ? t : head + (t - tail0); // its scalar slot otherwise
     const int t_slot = __builtin_amdgcn_readfirstlane(t_in_vec ? tv / THREADS : -1);
     const int t_thread = tv - (tv / THREADS) * THREADS;
     const int t_wave = __builtin_amdgcn_readfirstlane(t_thread / kWave);
@@ -109,7 +119,7 @@ __global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
                 for (int e = 0; e < h; ++e) p[e] += p[e + h];
             sz += (vi < nvec) ? (double)p[0] : 0.0;
         }
-        if (tid < ntail) sz += (double)ztail;
+        if (tid < nscal) sz += (double)ztail;
     }
 
     // ---- drop the target before any reduction ------------------------------
@@ -118,7 +128,7 @@ __global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
         for (int i = 0; i < NV; ++i)
             if (i == t_slot && t_lane_mine) v[i].kill(te);
     }
-    if (!t_in_vec && tid == t - tail0) ztail = ninf();
+    if (!t_in_vec && tid == t_scal) ztail = ninf();
 
 #pragma unroll
     for (int i = 0; i < NV; ++i) v[i].fence();
@@ -215,11 +225,11 @@ __global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
                     if (e == te) g[e] = c.gk;
             }
         }
-        if (vi < nvec) St::put(grow + vi * EPV * kOutSize, g);
+        if (vi < nvec) St::put(gvec + vi * EPV * kOutSize, g);
     }
-    if (tid < ntail) {
-        const float g = (!t_in_vec && tid == t - tail0) ? c.gk : grad_elem<OUT, LS>(ztail, c);
-        Store<OUT, 1>::put(grow + (tail0 + tid) * kOutSize, &g);
+    if (tid < nscal) {
+        const float g = (!t_in_vec && tid == t_scal) ? c.gk : grad_elem<OUT, LS>(ztail, c);
+        Store<OUT, 1>::put(grow + scol * kOutSize, &g);
     }
 }
 
@@ -529,9 +539,11 @@ static hipError_t launch_lds(const FusedArgs &a, int64_t T, int lds, hipStream_t
 }
 
 hipError_t launch_fused_resident(const FusedArgs &a, int in_dt, int out_dt, int64_t T,
-                                 hipStream_t stream) {
+                                 bool aligned, hipStream_t stream) {
     const bool ls = a.eps > 0.0f;
-    const int lds = ls ? 0 : lds_split_bytes(in_dt, a.V);
+    // the LDS-split kernel needs 16-byte aligned rows; rows that are not take
+    // the register-resident kernel, which peels their heads
+    const int lds = (ls || !aligned) ? 0 : lds_split_bytes(in_dt, a.V);
     if (lds > 0) {
         if (in_dt == CE_BF16)
             return out_dt == CE_BF16 ? launch_lds<CE_BF16, CE_BF16>(a, T, lds, stream)

@@ -155,7 +155,7 @@ hipError_t launch_reduce(const float *loss_rows, int64_t T, int reduction, const
 // dtype in_dt, or 0 if the row does not fit in registers.
 int resident_threads(int in_dt, int64_t V);
 hipError_t launch_fused_resident(const FusedArgs &a, int in_dt, int out_dt, int64_t T,
-                                 hipStream_t stream);
+                                 bool aligned, hipStream_t stream);
 // vec: 16-byte vectors (rows aligned) rather than single elements
 hipError_t launch_stats(const StatsArgs &a, int in_dt, bool vec, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
