@@ -102,6 +102,18 @@ def test_ragged_tail(V, dt):
     _fused_check(c, logits, target, what=f"ragged {dt} V={V}")
 
 
+@pytest.mark.parametrize("dt,V", [("bf16", 151936), ("bf16", 171776), ("bf16", 171784),
+                                  ("f32", 80000)])
+def test_long_rows_one_workgroup_per_cu(dt, V):
+    # beyond what two workgroups per CU hold, the register + LDS kernel runs
+    # one workgroup per CU (up to 171776 bf16 / 85888 fp32 columns); past
+    # that the rows stream
+    base = S.PAGE if dt == "bf16" else S.TINY
+    c, logits, target = _case(base, 520, V, 88 + V % 13)
+    target[5] = V - 1
+    _fused_check(c, logits, target, what=f"long rows {dt} V={V}")
+
+
 @pytest.mark.parametrize("eps", [0.0, 0.1])
 def test_rows_too_long_for_registers_bf16(eps):
     # bf16 rows longer than 131072 columns do not fit the resident kernels:

@@ -443,7 +443,8 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
         const bool split = p.T < kResidentMinRows && p.V_local >= kResidentSplitCols;
         const bool smoothed_long = p.label_smoothing > 0.0f && logits_dtype == CE_BF16 &&
                                    p.V_local > kSmoothedResidentMaxCols;
-        if (svec && !split && !smoothed_long && resident_threads(logits_dtype, p.V_local) > 0) {
+        if (svec && !split && !smoothed_long &&
+            fused_fits(logits_dtype, p.V_local, vec, p.label_smoothing > 0.0f)) {
             FusedArgs fa;
             fa.logits = logits;
             fa.ld = p.ld;

@@ -512,15 +512,24 @@ static hipError_t fused_dispatch(const FusedArgs &a, int64_t T, hipStream_t stre
 
 // LDS bytes per workgroup the split kernel needs for V columns (0 if the
 // row is not in its range).
+// Up to half of the 160 KB LDS (less the static part) two workgroups share a
+// CU; longer rows (to about 171K bf16 columns) run one workgroup per CU,
+// which still reads each row once, rather than stream it three times.
+constexpr int kLdsMaxBytes = 163840 - 512;
+
 static int lds_split_bytes(int in_dt, int64_t V) {
     const int64_t epv = (in_dt == CE_BF16) ? 8 : 4;
     const int64_t nvec = V / epv;
     const int64_t reg = (int64_t)kLdsRegSlots * kLdsThreads;
     if (nvec <= 8192 || nvec <= reg) return 0;
     const int64_t bytes = (nvec - reg) * 16;
-    // two workgroups per CU: half of the 160 KB LDS each, less the static part
-    if (bytes > 163840 / 2 - 512) return 0;
+    if (bytes > kLdsMaxBytes) return 0;
     return (int)bytes;
+}
+
+bool fused_fits(int in_dt, int64_t V, bool aligned, bool smoothing) {
+    if (aligned && !smoothing && lds_split_bytes(in_dt, V) > 0) return true;
+    return resident_threads(in_dt, V) > 0;
 }
 
 template <int IN, int OUT>
@@ -529,7 +538,7 @@ static hipError_t launch_lds(const FusedArgs &a, int64_t T, int lds, hipStream_t
     if (!configured) {
         const hipError_t e = hipFuncSetAttribute(
             (const void *)k_fused_lds<IN, OUT, kLdsRegSlots>,
-            hipFuncAttributeMaxDynamicSharedMemorySize, 163840 / 2 - 512);
+            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMaxBytes);
         if (e != hipSuccess) return e;
         configured = true;
     }

@@ -154,6 +154,9 @@ hipError_t launch_reduce(const float *loss_rows, int64_t T, int reduction, const
 // Threads x vectors per thread of the row-resident kernel for V columns of
 // dtype in_dt, or 0 if the row does not fit in registers.
 int resident_threads(int in_dt, int64_t V);
+// whether a fused kernel takes rows of V columns (aligned: 16-byte aligned
+// rows; smoothing: label smoothing on)
+bool fused_fits(int in_dt, int64_t V, bool aligned, bool smoothing);
 hipError_t launch_fused_resident(const FusedArgs &a, int in_dt, int out_dt, int64_t T,
                                  bool aligned, hipStream_t stream);
 // vec: 16-byte vectors (rows aligned) rather than single elements
