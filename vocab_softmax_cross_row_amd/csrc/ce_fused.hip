@@ -534,14 +534,10 @@ bool fused_fits(int in_dt, int64_t V, bool aligned, bool smoothing) {
 
 template <int IN, int OUT>
 static hipError_t launch_lds(const FusedArgs &a, int64_t T, int lds, hipStream_t stream) {
-    static bool configured = false;
-    if (!configured) {
-        const hipError_t e = hipFuncSetAttribute(
-            (const void *)k_fused_lds<IN, OUT, kLdsRegSlots>,
-            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMaxBytes);
-        if (e != hipSuccess) return e;
-        configured = true;
-    }
+    static std::atomic<bool> configured[kMaxDevices];
+    const hipError_t e =
+        raise_lds_once((const void *)k_fused_lds<IN, OUT, kLdsRegSlots>, kLdsMaxBytes, configured);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_fused_lds<IN, OUT, kLdsRegSlots>), dim3((unsigned)T), dim3(kLdsThreads),
                        lds, stream, a);
     return hipGetLastError();

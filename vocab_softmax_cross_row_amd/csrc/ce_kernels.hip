@@ -729,14 +729,11 @@ hipError_t launch_stats(const StatsArgs &a, int in_dt, bool vec, hipStream_t str
         // as many workgroups as the device holds at once, with the units
         // spread evenly over them
         auto kern = k_stats_tab<kStreamThreads, kStreamUnroll>;
-        int dev = 0, cus = 0, per_cu = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e == hipSuccess)
-            e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)kern, kStreamThreads, 0);
+        static std::atomic<int> slot_cache[kMaxDevices];
+        int64_t slots = 0;
+        const hipError_t e = device_slots((const void *)kern, kStreamThreads, 0, slot_cache, &slots);
         if (e != hipSuccess) return e;
         const int64_t units = a.T * a.nchunks;
-        const int64_t slots = std::max<int64_t>(1, (int64_t)cus * std::max(per_cu, 1));
         const int64_t per_wg = (units + slots - 1) / slots;
         const int64_t wgs = (units + per_wg - 1) / per_wg;
         hipLaunchKernelGGL(kern, dim3((unsigned)wgs), dim3(kStreamThreads), 0, stream, a, a.exp_tab);

@@ -5,9 +5,56 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "vocab_ce.h"
 
 namespace vce {
+
+// ---------------------------------------------------------------------------
+// Per-device launch facts, computed once per device (host side).
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+
+inline hipError_t current_device(int *dev) {
+    hipError_t e = hipGetDevice(dev);
+    if (e == hipSuccess && (*dev < 0 || *dev >= kMaxDevices)) e = hipErrorInvalidDevice;
+    return e;
+}
+
+// Workgroups of `kern` (threads per workgroup, dynamic LDS bytes) the current
+// device holds at once: its CUs times the kernel's occupancy per CU; `cache`
+// has one entry per device.
+inline hipError_t device_slots(const void *kern, int threads, size_t lds, std::atomic<int> *cache,
+                               int64_t *slots) {
+    int dev = 0;
+    hipError_t e = current_device(&dev);
+    if (e != hipSuccess) return e;
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
+        int cus = 0, per_cu = 0;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, lds);
+        if (e != hipSuccess) return e;
+        v = std::max(cus, 1) * std::max(per_cu, 1);
+        cache[dev].store(v, std::memory_order_relaxed);
+    }
+    *slots = v;
+    return hipSuccess;
+}
+
+// Raises `kern`'s dynamic LDS ceiling to `bytes`, once per device.
+inline hipError_t raise_lds_once(const void *kern, int bytes, std::atomic<bool> *done) {
+    int dev = 0;
+    hipError_t e = current_device(&dev);
+    if (e != hipSuccess) return e;
+    if (done[dev].load(std::memory_order_relaxed)) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done[dev].store(true, std::memory_order_relaxed);
+    return e;
+}
+
 
 struct FusedArgs {
     const void *logits;

@@ -717,24 +717,17 @@ hipError_t launch_linear_rowconst(const LinRowArgs &a, hipStream_t stream) {
 
 template <int EPI, bool LS>
 static hipError_t gemm_launch(const GemmArgs &g, hipStream_t stream) {
-    static bool attr = false;
-    if (!attr) {
-        hipError_t e = hipFuncSetAttribute((const void *)k_gemm<EPI, LS>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           kGemmLdsBytes);
-        if (e != hipSuccess) return e;
-        attr = true;
-    }
+    static std::atomic<bool> attr[kMaxDevices];
+    static std::atomic<int> slot_cache[kMaxDevices];
+    const void *kern = (const void *)k_gemm<EPI, LS>;
+    hipError_t e = raise_lds_once(kern, kGemmLdsBytes, attr);
+    if (e != hipSuccess) return e;
     // as many workgroups as the device holds at once, a multiple of 8
-    int dev = 0, cus = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)k_gemm<EPI, LS>, kGT,
-                                                         kGemmLdsBytes);
+    int64_t held = 0;
+    e = device_slots(kern, kGT, kGemmLdsBytes, slot_cache, &held);
     if (e != hipSuccess) return e;
     const int64_t ids = tile_ids(g.tiles_m, g.tiles_n);
-    const int64_t slots = std::max<int64_t>(kXcds, (int64_t)cus * std::max(per_cu, 1) / kXcds * kXcds);
+    const int64_t slots = std::max<int64_t>(kXcds, held / kXcds * kXcds);
     const dim3 grid((unsigned)(kGemmPersistent<EPI> ? std::min(ids, slots) : ids));
     hipLaunchKernelGGL((k_gemm<EPI, LS>), grid, dim3(kGT), kGemmLdsBytes, stream, g);
     return hipGetLastError();
