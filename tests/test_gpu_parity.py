@@ -296,6 +296,39 @@ def test_split_vocabulary_shards(cuts, eps, T):
         P.assert_grad_close(g, ref["grad"][:, a:b], f"shard grad [{a},{b})")
 
 
+@pytest.mark.parametrize("dt,V,a,eps", [("bf16", 64128, 0, 0.1), ("bf16", 64128, 64128, 0.0),
+                                        ("bf16", 40003, 17, 0.1), ("f32", 20001, 3, 0.0)])
+def test_backward_long_chunks(dt, V, a, eps):
+    """Backward over rows long enough for the 1024-thread gradient shape
+    (one column chunk per row once T >= 1024), for a shard of a wider
+    vocabulary at an aligned or odd column offset; the gradient goes into a
+    larger canary-filled buffer, which must keep its canary outside the
+    [T, V] view."""
+    T, Vt = 1030, a + V + 5
+    base = S.PAGE if dt == "bf16" else S.TINY
+    c, whole, target = _case(base, T, Vt, 610 + V % 89, eps=eps)
+    logits = whole[:, a:a + V]
+    _say(f"[long chunks] T={T} shard [{a},{a + V}) of {Vt} {dt} eps={eps}")
+    # row constants of the whole vocabulary, then this shard's backward
+    m = vce.forward(whole, target, label_smoothing=eps)
+    out_dt = logits.dtype
+    canary = 0x7FC5 if out_dt == torch.bfloat16 else 0x7FC00005
+    ity = torch.int16 if out_dt == torch.bfloat16 else torch.int32
+    # same residue mod 16 bytes as the logits view, so the vector path runs
+    buf = torch.full((T + 1, Vt), canary, dtype=ity, device=DEV).view(out_dt)
+    g = buf[:T, a:a + V]
+    vce.backward(logits, target, m["fin"], m["n_valid"], vocab_start=a, V_total=Vt,
+                 label_smoothing=eps, grad=g)
+    torch.cuda.synchronize()
+    raw = buf.view(ity)
+    assert torch.all(raw[:T, :a] == canary), "write before the start of a row"
+    assert torch.all(raw[:T, a + V:] == canary), "write past the end of a row"
+    assert torch.all(raw[T] == canary), "write past the last row"
+    # the oracle over the whole vocabulary; compare this shard's columns
+    ref = P.oracle_for(whole, target, eps=eps)
+    P.assert_grad_close(g, ref["grad"][:, a:a + V], f"long chunks [{a},{a + V})")
+
+
 def test_fused_equals_unfused_equals_shards_loss():
     """Three paths to the same loss (fp32 rounding apart)."""
     c, logits, target = _case(S.PAGE, 600, 64128, 99)
