@@ -108,3 +108,21 @@ def test_split_vocabulary_full_size(page):
     P.assert_grad_close(g2[idx], ref["grad"][:, half:], "split shard 1")
     lr = m["loss_rows"].double().cpu().numpy()
     assert abs(m["loss"].item() - lr.sum() / n_valid) <= 1e-6 * abs(m["loss"].item())
+
+
+def test_mid_workload_full_size():
+    """T = 4096, V = 32000 bf16 logits ~ N(0, 2^2), 82 ignored rows, mean,
+    bf16 gradient: every loss and every gradient element against the
+    oracle over the whole batch (it finishes in seconds at this size)."""
+    c = S.MID
+    print(f"[full] mid workload T={c.T} V={c.V}", flush=True)
+    logits, target = S.generate(c, device=DEV, block_rows=1024)
+    lg, tg = logits, target
+    out = vce.fused_fwd_bwd(lg, tg)
+    torch.cuda.synchronize()
+    ref = P.oracle_for(lg, tg)
+    assert int(out["n_valid"].item()) == ref["n_valid"] == c.T - c.n_ignored
+    assert int(out["err_count"].item()) == 0
+    P.assert_loss_rows(out["loss_rows"], ref, "mid full size")
+    P.assert_scalar_loss(out["loss"].item(), ref["loss"], "mid full size")
+    P.assert_grad_close(out["grad"], ref["grad"], "mid full size grad")
