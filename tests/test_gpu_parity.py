@@ -241,9 +241,11 @@ def _stats_check(gpu_stats, ref_stats, target, V_total, what, eps):
     assert np.all(st["own"][skip] == 0) and np.all(st["zt"][skip] == 0)
 
 
-@pytest.mark.parametrize("eps", [0.0, 0.1])
-def test_forward_backward_unsharded(eps):
-    c, logits, target = _case(S.PAGE, 1100, 20000, 91, eps=eps)
+@pytest.mark.parametrize("V,eps", [(20000, 0.0), (20000, 0.1), (40003, 0.0), (64128, 0.0)])
+def test_forward_backward_unsharded(V, eps):
+    # 40003 and 64128 columns: rows long enough for the 128-thread
+    # statistics shape (odd width: a peeled head)
+    c, logits, target = _case(S.PAGE, 1100, V, 91, eps=eps)
     _say(f"[unfused] T={c.T} V={c.V} eps={eps}")
     f = vce.forward(logits, target, label_smoothing=eps)
     g = vce.backward(logits, target, f["fin"], f["n_valid"], label_smoothing=eps)

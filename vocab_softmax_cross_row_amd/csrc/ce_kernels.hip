@@ -170,7 +170,7 @@ __device__ __forceinline__ void stats_online(const char *zrow, int64_t c0, int64
         for (int u = 0; u < UNROLL; ++u) {
             const int64_t vi = base + (int64_t)u * THREADS + tid;
             if (vi < nv)
-                v[u].load(zrow + (v0 + vi * EPV) * In::kSize);
+                v[u].template load<true>(zrow + (v0 + vi * EPV) * In::kSize);
             else
                 v[u].fill_ninf();
         }
@@ -706,10 +706,22 @@ hipError_t launch_reduce(const float *loss_rows, int64_t T, int reduction, const
 constexpr int kStreamThreads = 256;
 constexpr int kStreamUnroll = 4;
 
+// Long chunks without smoothing: 128 threads x 16 vectors per thread, more
+// rows in flight per CU and a cheaper workgroup reduction (16384 x 128256
+// bf16 forward: 723 -> 631 us against 256 x 4 with default loads; 256 x 8:
+// 669, 64 x 16: 644).  The smoothed online form (fp64 exponentials) would
+// need 200+ VGPRs in this shape and keeps 256 x 4.
+constexpr int kLongStatsThreads = 128;
+constexpr int kLongStatsUnroll = 16;
+constexpr int64_t kLongStatsMinVecs = 4096;
+
 template <int IN, bool LS>
 static void stats_dispatch(const StatsArgs &a, bool vec, dim3 grid, hipStream_t stream) {
     constexpr int EPV = Elem<IN>::kVec;
-    if (vec)
+    if (!LS && vec && a.chunk_cols / EPV >= kLongStatsMinVecs)
+        hipLaunchKernelGGL((k_stats<IN, EPV, kLongStatsThreads, kLongStatsUnroll, LS>), grid,
+                           dim3(kLongStatsThreads), 0, stream, a);
+    else if (vec)
         hipLaunchKernelGGL((k_stats<IN, EPV, kStreamThreads, kStreamUnroll, LS>), grid,
                            dim3(kStreamThreads), 0, stream, a);
     else
