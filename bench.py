@@ -23,6 +23,10 @@ Extra objects in the line:
   split_v       the vocabulary split in two 64128-column shards with label
                 smoothing 0.1: ce_forward per shard, ce_merge_shard_stats,
                 ce_backward per shard, timed the same way.
+  unfused       the same batch through ce_forward (whole vocabulary: row
+                statistics, finalize, loss) and then ce_backward, no
+                smoothing; bytes: one read for the forward, a read and a
+                write for the backward.
   linear_ce     cross-entropy of a linear classifier without stored logits
                 (ce_linear_fwd_bwd): E [8192, 2048] and C [128256, 2048] bf16,
                 loss + dE + dC; MFMA roofline: 4 products of 2 N V D flops
@@ -120,6 +124,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-split", action="store_true", help="skip the split-V measurement")
     ap.add_argument("--no-linear", action="store_true", help="skip the linear-classifier run")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="skip the separate forward / backward measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain copy of known size (for counter scaling)")
     args = ap.parse_args()
@@ -215,6 +221,51 @@ def main():
                  "algorithmic_bytes": sb, "frac_of_peak": round(sb / (sms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
         print(f"# split-V: {sms:.4f} ms/step", file=sys.stderr, flush=True)
 
+    unfused = None
+    if not args.no_unfused:
+        # the same batch through the separate calls: ce_forward over the whole
+        # vocabulary (statistics, finalize, loss), then ce_backward
+        pu = B.make_problem(T, V, ignore_index=case.ignore_index, reduction="mean")
+        nuw = B.ce_workspace_bytes(pu, B.CE_OP_FORWARD)
+        wsu = torch.empty(max(nuw, 1), dtype=torch.uint8, device=dev)
+        ustats = torch.empty((T, B.ROW_STATS_BYTES), dtype=torch.uint8, device=dev)
+        ufin = torch.empty((T, B.ROW_FINAL_BYTES), dtype=torch.uint8, device=dev)
+
+        def fwd_only():
+            B.ce_forward(pu, logits, B.CE_BF16, target, ustats, ufin, loss_rows, loss, n_valid,
+                         err, wsu, nuw, stream)
+
+        def bwd_only():
+            B.ce_backward(pu, logits, B.CE_BF16, target, ufin, n_valid, None, grad, B.CE_BF16, V,
+                          stream)
+
+        ku = max(1, args.steps // 5)
+        times = {}
+        for name, fn in (("forward", fwd_only), ("backward", bwd_only)):
+            for _ in range(max(1, args.warmup // 2)):
+                fn()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(ku):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[name] = e0.elapsed_time(e1) / ku
+        fb, bb = T * V * 2, T * V * 4
+        unfused = {"workload": "ce_forward (whole vocabulary) then ce_backward, no smoothing",
+                   "steps": ku,
+                   "forward_ms": round(times["forward"], 4),
+                   "forward_GB/s": round(fb / (times["forward"] * 1e-3) / 1e9, 1),
+                   "forward_frac_of_peak": round(fb / (times["forward"] * 1e-3) / 1e9
+                                                 / PEAK_HBM_GBS, 4),
+                   "backward_ms": round(times["backward"], 4),
+                   "backward_GB/s": round(bb / (times["backward"] * 1e-3) / 1e9, 1),
+                   "backward_frac_of_peak": round(bb / (times["backward"] * 1e-3) / 1e9
+                                                  / PEAK_HBM_GBS, 4),
+                   "forward_bytes": fb, "backward_bytes": bb}
+        print(f"# unfused: forward {times['forward']:.4f} ms, backward {times['backward']:.4f} ms",
+              file=sys.stderr, flush=True)
+
     linear = None
     if not args.no_linear:
         lc = S.LINEAR
@@ -285,6 +336,7 @@ def main():
                      "traffic": counter_traffic(), "algorithmic_bytes": nbytes},
         "cpu_baseline": cpu,
         "split_v": split,
+        "unfused": unfused,
         "linear_ce": linear,
     }
     print(json.dumps(out), flush=True)
