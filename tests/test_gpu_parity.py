@@ -497,15 +497,13 @@ def test_writes_stay_inside_the_gradient_rows(T, V, in_dt, out_dt):
     P.assert_loss_rows(out["loss_rows"], ref, "canary")
 
 
-@pytest.mark.parametrize("shard", [False, True])
-def test_smoothed_bf16_statistics_edge_values(shard):
-    """The smoothed bf16 statistics read e^z from a table of bf16 patterns
-    with 2^-16 <= |z| < 2^9: zeros and values below 2^-16 take a series,
-    values of magnitude >= 512 send the chunk to the online form, -inf
-    logits and the target read the table's zero entry."""
-    c, logits, target = _case(S.PAGE, 64, 5000, 131, eps=0.1)
+def _table_edge_rows(logits, target):
+    """Rows 0-7 rewritten with the values the table of e^z treats apart:
+    zeros, |z| around 2^-16, |z| >= 512, -inf, a tiny-valued row, values
+    just below 512 and +-1000."""
     z = logits.float().cpu()
     t = target.cpu()
+
     def put(r, cols, vals):
         for col, v in zip(cols, vals):
             if int(t[r]) != col:
@@ -518,7 +516,29 @@ def test_smoothed_bf16_statistics_edge_values(shard):
     z[5] *= 1e-6
     put(6, [30, 31, 32], [510.0, -510.0, 511.0])
     put(7, [1, 2], [-1000.0, 1000.0])
-    logits = z.to(torch.bfloat16).to(DEV)
+    return z.to(torch.bfloat16).to(DEV)
+
+
+@pytest.mark.parametrize("V", [12000, 30001])
+def test_smoothed_fused_table_edge_values(V):
+    """Fused forward + backward of smoothed bf16 rows with 16384 < V <= 32768
+    (the row-resident kernel that sums e^z from the LDS table; 30001: an odd
+    width, so rows have a peeled head and a scalar tail), and 12000 (fp64
+    exponentials), on the table's edge values."""
+    c, logits, target = _case(S.PAGE, 64, V, 137, eps=0.1)
+    logits = _table_edge_rows(logits, target)
+    _fused_check(c, logits, target, what=f"table edges fused V={V}")
+
+
+@pytest.mark.parametrize("shard", [False, True])
+def test_smoothed_bf16_statistics_edge_values(shard):
+    """The smoothed bf16 statistics read e^z from a table of bf16 patterns
+    with 2^-16 <= |z| < 2^9: zeros and values below 2^-16 take a series,
+    values of magnitude >= 512 send the chunk to the online form, -inf
+    logits and the target read the table's zero entry."""
+    c, logits, target = _case(S.PAGE, 64, 5000, 131, eps=0.1)
+    logits = _table_edge_rows(logits, target)
+    t = target.cpu()
     eps = 0.1
     ref = P.oracle_for(logits, target, eps=eps)
     if shard:
@@ -539,19 +559,21 @@ def test_smoothed_bf16_statistics_edge_values(shard):
     P.assert_grad_close(g, ref["grad"], "table edges grad")
 
 
+@pytest.mark.parametrize("V", [6144, 24576])
 @pytest.mark.parametrize("eps", [0.1, 0.6])
-def test_smoothed_gradient_where_p_meets_eps_over_v(eps):
+def test_smoothed_gradient_where_p_meets_eps_over_v(eps, V):
     """With smoothing, a non-target gradient is k (p_j - eps/V), which cancels
     where p_j is close to eps/V.  Each row holds 4096 zeros and a sweep of
     2048 logits through [-3, 1] (shifted a little per row), so that p_j
     passes eps/V in bf16 steps: some entries fall inside the window where the
     difference is rebuilt from log2(p/u) (|log2(p/u)| < 2^-6), many just
-    outside it, where the plain form must already be within a bf16 ulp."""
-    T, V = 8, 6144
+    outside it, where the plain form must already be within a bf16 ulp.
+    V = 24576 takes the fused kernel that sums e^z from the LDS table."""
+    T = 8
     z = torch.zeros(T, V)
     sweep = torch.linspace(-3.0, 1.0, 2048)
     for r in range(T):
-        z[r, 4096:] = sweep + r * 2.0 ** -9
+        z[r, V - 2048:] = sweep + r * 2.0 ** -9
     logits = z.to(torch.bfloat16).to(DEV)
     target = torch.tensor([17 * (r + 1) for r in range(T)], dtype=torch.int64, device=DEV)
     zz = logits.double().cpu().numpy()

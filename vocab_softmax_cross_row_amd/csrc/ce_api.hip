@@ -458,6 +458,13 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
             fa.loss_rows = lr;
             fa.reduction = p.reduction;
             fa.eps = p.label_smoothing;
+            fa.exp_tab = nullptr;
+            if (p.label_smoothing > 0.0f && fused_table(logits_dtype, p.V_local)) {
+                // the smoothed sums read e^z from a table (built per call)
+                double *tab = at<double>(ws, l.exp_tab);
+                VCE_TRY(launch_exp_table(tab, s));
+                fa.exp_tab = tab;
+            }
             VCE_TRY(launch_fused_resident(fa, logits_dtype, grad_dtype, p.T, vec, s));
         } else {
             // streaming: stats (column chunks) -> merge + finalize -> gradient

@@ -26,23 +26,78 @@ namespace vce {
 // fused, row resident
 // ===========================================================================
 
-// One workgroup per row; the row lives in registers from its load to its
-// gradient store.  FAST = bf16 gradient without smoothing: fp32 finalize
-// and the biased exponent form (see GradConst); otherwise fp64 finalize.
-template <int IN, int OUT, int THREADS, int NV, bool LS>
-__global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// e^z of one bf16 pattern b from the LDS table of e^z (see kExpTabLo): the
+// table's entry, 0 for -inf, 1 + z + z^2/2 for |z| < 2^-16 (error below
+// 1e-15); |z| >= 512, +inf and NaN set `bad` (the caller recomputes).
+__device__ __forceinline__ double tab_exp1(uint32_t b, const double *tab, bool &bad) {
+    const uint32_t mag = b & 0x7fffu;
+    const uint32_t off = mag - kExpTabLo;
+    if (off < (uint32_t)kExpTabHalf) return tab[2 * off + (b >> 15)];
+    if (b == 0xff80u) return 0.0;
+    if (mag < kExpTabLo) {
+        const double z = (double)__uint_as_float(b << 16);
+        return 1.0 + z * (1.0 + 0.5 * z);
+    }
+    bad = true;
+    return 0.0;
+}
+
+// Sum of e^z over the 8 bf16 logits of one 16-byte vector, from the table.
+// Two logits per 32-bit word: byte offset 16 (|pattern| - kExpTabLo),
+// clamped to the zero entries, plus 8 for a negative logit; all 8 table
+// reads are issued together.  Returns false (and a sum to be ignored) when
+// a pattern lies outside the table: the killed target, padding, |z| < 2^-16
+// or |z| >= 512; tab_exp8_slow then takes the vector logit by logit.
+__device__ __forceinline__ bool tab_exp8(const u32x4 &w, const double *tab, double &sum) {
+    const char *tabc = reinterpret_cast<const char *>(tab);
+    u16x2 omax = {0, 0};
+    double t[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const u16x2 off =
+            __builtin_bit_cast(u16x2, w[q] & 0x7fff7fffu) - (u16x2)(uint16_t)kExpTabLo;
+        omax = __builtin_elementwise_max(omax, off);
+        const u16x2 c = __builtin_elementwise_min(off, (u16x2)(uint16_t)kExpTabHalf);
+        const uint32_t a2 =
+            __builtin_bit_cast(uint32_t, c << (uint16_t)4) | ((w[q] >> 12) & 0x00080008u);
+        t[2 * q] = *reinterpret_cast<const double *>(tabc + (a2 & 0xffffu));
+        t[2 * q + 1] = *reinterpret_cast<const double *>(tabc + (a2 >> 16));
+    }
+    sum = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
+    return omax.x < (uint16_t)kExpTabHalf && omax.y < (uint16_t)kExpTabHalf;
+}
+
+__device__ __forceinline__ double tab_exp8_slow(const u32x4 &w, const double *tab, bool &bad) {
+    double s = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t x = w[e >> 1];
+        s += tab_exp1((e & 1) ? (x >> 16) : (x & 0xffffu), tab, bad);
+    }
+    return s;
+}
+
+// One row, resident in registers from its load to its gradient store; the
+// workgroup's threads all call it.  FAST = bf16 gradient without smoothing:
+// fp32 finalize and the biased exponent form (see GradConst); otherwise
+// fp64 finalize.  TAB (bf16 with smoothing): the fp64 sum of exponentials
+// reads e^z from the LDS table `tab` instead of an fp64 exponential per
+// logit.
+template <int IN, int OUT, int THREADS, int NV, bool LS, bool TAB>
+__device__ __forceinline__ void fused_row(const FusedArgs &a, int64_t row,
+                                          BlockRed<THREADS> &red, GradConst &gc_sh,
+                                          const double *tab) {
     using In = Elem<IN>;
     constexpr int EPV = In::kVec;
     using Ch = Chunk<IN, EPV>;
     using St = Store<OUT, EPV, true>;
     constexpr int kOutSize = (OUT == CE_BF16) ? 2 : 4;
     constexpr bool FAST = (OUT == CE_BF16) && !LS;
-
-    __shared__ BlockRed<THREADS> red;
-    __shared__ GradConst gc_sh;
+    static_assert(!TAB || (LS && IN == CE_BF16), "the table holds e^z of bf16 logits");
 
     const int tid = threadIdx.x;
-    const int64_t row = xcd_major(blockIdx.x, gridDim.x);
     const int V = (int)a.V;
     const char *zrow = static_cast<const char *>(a.logits) + row * a.ld * In::kSize;
     char *grow = static_cast<char *>(a.grad) + row * a.ldg * kOutSize;
@@ -88,6 +143,21 @@ __global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
     }
     float ztail = ninf(); // this thread's scalar slot
     if (tid < nscal) ztail = In::load1(zrow + scol * In::kSize);
+    if constexpr (TAB) {
+        // the table of e^z: global -> LDS directly (no registers), behind
+        // the row's loads; waited for just before the sum of exponentials
+        constexpr int kTabVecs = (kExpTabN * 8 + 15) / 16;
+        const __amdgpu_buffer_rsrc_t rt =
+            __builtin_amdgcn_make_buffer_rsrc((void *)a.exp_tab, 0, kExpTabN * 8, 0x00020000);
+        const int wave_base = __builtin_amdgcn_readfirstlane((tid / kWave) * kWave);
+        u32x4 *tv = reinterpret_cast<u32x4 *>(const_cast<double *>(tab));
+#pragma unroll 1
+        for (int q = 0; q * THREADS < kTabVecs; ++q)
+            if (q * THREADS + tid < kTabVecs)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rt, (__attribute__((address_space(3))) void *)(tv + q * THREADS + wave_base), 16,
+                    (q * THREADS + tid) * 16, 0, 0, 0);
+    }
 
     // where the target sits: vector tv = slot t_slot of thread t_thread
     // (wave t_wave), element te; or the scalar tail.  t is the same for the
@@ -149,14 +219,48 @@ __global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
     if constexpr (LS) {
         // With smoothing the gradient k (p_j - eps/V) cancels where p_j is
         // close to eps/V and magnifies any error of lse there, so the sum is
-        // taken with fp64 exponentials and fp64 accumulation.
-        if (mx != ninf()) {
-            const double md = (double)mx;
+        // taken with fp64 exponentials (or table entries) and fp64
+        // accumulation.
+        bool online = !TAB;
+        if constexpr (TAB) {
+            // unshifted: sum of e^z (fp64 spans e^-512 .. e^512), then times
+            // e^-mx (-mx is a bf16 value: mx is a max of bf16 logits)
+            __builtin_amdgcn_s_waitcnt(0); // this wave's part of the table has landed
+            __syncthreads();               // and every other wave's
+            if (mx != ninf()) {
+                bool bad = false;
+                // branch-free table sums first; vectors with a pattern outside
+                // the table are marked and summed logit by logit afterwards
+                uint32_t slow = 0;
 #pragma unroll
-            for (int i = 0; i < NV; ++i)
+                for (int i = 0; i < NV; ++i) {
+                    double si;
+                    const bool ok = tab_exp8(v[i].v, tab, si);
+                    sd += ok ? si : 0.0;
+                    slow |= (ok ? 0u : 1u) << i;
+                }
+                if (slow) {
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) sd += exp_nonpos((double)v[i].get(e) - md);
-            sd += exp_nonpos((double)ztail - md);
+                    for (int i = 0; i < NV; ++i)
+                        if ((slow >> i) & 1u) sd += tab_exp8_slow(v[i].v, tab, bad);
+                }
+                sd += tab_exp1(__float_as_uint(ztail) >> 16, tab, bad);
+                sd *= tab_exp1((__float_as_uint(mx) >> 16) ^ 0x8000u, tab, bad);
+                online = block_max<THREADS>(bad ? 1.0f : 0.0f, red, 1) > 0.0f;
+            }
+        }
+        if (online) {
+            // |z| >= 512, +inf or NaN somewhere in the row (TAB): the whole
+            // row again with fp64 exponentials
+            sd = 0.0;
+            if (mx != ninf()) {
+                const double md = (double)mx;
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) sd += exp_nonpos((double)v[i].get(e) - md);
+                sd += exp_nonpos((double)ztail - md);
+            }
         }
         sd = block_sum_d<THREADS>(sd, red, 0);
         sz = block_sum_d<THREADS>(sz, red, 1);
@@ -231,6 +335,32 @@ __global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
         const float g = (!t_in_vec && tid == t_scal) ? c.gk : grad_elem<OUT, LS>(ztail, c);
         Store<OUT, 1>::put(grow + scol * kOutSize, &g);
     }
+}
+
+template <int IN, int OUT, int THREADS, int NV, bool LS>
+__global__ __launch_bounds__(THREADS) void k_fused_resident(FusedArgs a) {
+    __shared__ BlockRed<THREADS> red;
+    __shared__ GradConst gc_sh;
+    fused_row<IN, OUT, THREADS, NV, LS, false>(a, xcd_major(blockIdx.x, gridDim.x), red, gc_sh,
+                                               nullptr);
+}
+
+// bf16 rows with smoothing, 16384 < V <= 32768: one row per workgroup, as
+// k_fused_resident, with the table of e^z (51 KB, read from L2 by each
+// workgroup) in LDS.  The table allows 3 workgroups per CU, so registers are
+// capped for 3 waves per SIMD.  A persistent form (the table loaded once per
+// workgroup, rows in a loop) kept row-loop invariants in registers: 129 VGPRs
+// before any of the row.
+constexpr int kTabThreads = 256;
+
+template <int OUT, int NV>
+__global__ __launch_bounds__(kTabThreads) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void k_fused_resident_tab(FusedArgs a) {
+    __shared__ BlockRed<kTabThreads> red;
+    __shared__ GradConst gc_sh;
+    __shared__ u32x4 tab[(kExpTabN * 8 + 15) / 16];
+    fused_row<CE_BF16, OUT, kTabThreads, NV, true, true>(a, xcd_major(blockIdx.x, gridDim.x), red,
+                                                         gc_sh, reinterpret_cast<const double *>(tab));
 }
 
 // ===========================================================================
@@ -527,6 +657,12 @@ static int lds_split_bytes(int in_dt, int64_t V) {
     return (int)bytes;
 }
 
+bool fused_table(int in_dt, int64_t V) {
+    const int i = resident_index(in_dt, V);
+    return in_dt == CE_BF16 && i >= 0 && kResident[i].threads == kTabThreads &&
+           kResident[i].nv == 16;
+}
+
 bool fused_fits(int in_dt, int64_t V, bool aligned, bool smoothing) {
     if (aligned && !smoothing && lds_split_bytes(in_dt, V) > 0) return true;
     return resident_threads(in_dt, V) > 0;
@@ -543,9 +679,25 @@ static hipError_t launch_lds(const FusedArgs &a, int64_t T, int lds, hipStream_t
     return hipGetLastError();
 }
 
+template <int OUT>
+static hipError_t tab_dispatch(const FusedArgs &a, int64_t T, hipStream_t stream) {
+    hipLaunchKernelGGL((k_fused_resident_tab<OUT, 16>), dim3((unsigned)T), dim3(kTabThreads), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_fused_resident(const FusedArgs &a, int in_dt, int out_dt, int64_t T,
                                  bool aligned, hipStream_t stream) {
     const bool ls = a.eps > 0.0f;
+    if (ls && in_dt == CE_BF16 && a.exp_tab) {
+        // smoothed bf16 rows of the 256 x 16 shape (16384 < V <= 32768):
+        // sums from the table.  Shorter rows keep fp64 exponentials: with
+        // 256 x 8 (V <= 16384) the table, read per row, cost more than it
+        // saved (32768 x 12000: 532 -> 601 us; 65536 x 32000: 2216 -> 1896)
+        if (fused_table(in_dt, a.V))
+            return out_dt == CE_BF16 ? tab_dispatch<CE_BF16>(a, T, stream)
+                                     : tab_dispatch<CE_F32>(a, T, stream);
+    }
     // the LDS-split kernel needs 16-byte aligned rows; rows that are not take
     // the register-resident kernel, which peels their heads
     const int lds = (ls || !aligned) ? 0 : lds_split_bytes(in_dt, a.V);

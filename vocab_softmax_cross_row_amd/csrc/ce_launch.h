@@ -69,6 +69,9 @@ struct FusedArgs {
     float *loss_rows;
     int reduction;
     float eps;
+    // smoothing, bf16 rows: e^z per bf16 pattern (kExpTabN entries, built by
+    // launch_exp_table), or NULL for fp64 exponentials
+    const double *exp_tab = nullptr;
 };
 
 struct StatsArgs {
@@ -204,6 +207,9 @@ int resident_threads(int in_dt, int64_t V);
 // whether a fused kernel takes rows of V columns (aligned: 16-byte aligned
 // rows; smoothing: label smoothing on)
 bool fused_fits(int in_dt, int64_t V, bool aligned, bool smoothing);
+// whether the row-resident kernel with smoothing sums e^z from the table
+// (FusedArgs::exp_tab) for rows of V columns of dtype in_dt
+bool fused_table(int in_dt, int64_t V);
 hipError_t launch_fused_resident(const FusedArgs &a, int in_dt, int out_dt, int64_t T,
                                  bool aligned, hipStream_t stream);
 // vec: 16-byte vectors (rows aligned) rather than single elements
