@@ -154,6 +154,18 @@ def test_label_smoothing_fp32_out():
     _fused_check(c, logits, target, what="smoothing fp32 sum")
 
 
+@pytest.mark.parametrize("reduction", ["sum", "none"])
+def test_label_smoothing_bf16_in_fp32_out_table(reduction):
+    # bf16 rows of 16385 to 32768 columns with smoothing: the fused kernel
+    # that sums e^z from the LDS table, writing an fp32 gradient
+    c, logits, target = _case(S.PAGE, 300, 24000, 63, eps=0.2, reduction=reduction)
+    go = None
+    if reduction == "none":
+        go = torch.linspace(-2.0, 2.0, c.T, device=DEV)
+    _fused_check(c, logits, target, grad_dtype=torch.float32, grad_output=go,
+                 what=f"smoothing bf16 -> fp32, {reduction}")
+
+
 def test_split_v_grid_short_T():
     """Few rows, long rows: the fused entry point splits every row into
     column chunks (partial statistics merged on the device)."""
