@@ -644,3 +644,46 @@ def test_in_place_backward_on_shards():
     torch.cuda.synchronize()
     assert torch.equal(buf[:, :cut].view(torch.int16), ref[0].view(torch.int16))
     assert torch.equal(buf[:, cut:].view(torch.int16), ref[1].view(torch.int16))
+
+
+# --------------------------------------------------------------------------
+# HIP graph capture: a captured call replays like an eager one
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("V,eps", [(128256, 0.0), (24000, 0.1), (150001, 0.1)])
+def test_graph_replay_matches_eager(V, eps):
+    """The library allocates nothing, never synchronises and launches only
+    on the caller's stream, so a call can be captured into a HIP graph.
+    Each replay (with new logits copied into the captured input between
+    replays, eagerly) must equal an eager call on the same bytes, bit for
+    bit: the fused register + LDS kernel, the smoothed table kernel, and the
+    streaming path (column-chunk statistics, merge, gradient)."""
+    T = 300
+    cases = [_case(S.PAGE, T, V, 700 + k, eps=eps) for k in range(3)]
+    x = cases[0][1].clone()
+    tg = cases[0][2].clone()
+    # warm-up outside the capture (per-device launch caches, LDS limits)
+    vce.fused_fwd_bwd(x, tg, label_smoothing=eps)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            out = vce.fused_fwd_bwd(x, tg, label_smoothing=eps)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for k, (c, logits, target) in enumerate(cases):
+        x.copy_(logits)
+        tg.copy_(target)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = vce.fused_fwd_bwd(logits, target, label_smoothing=eps)
+        torch.cuda.synchronize()
+        _say(f"[graph] V={V} eps={eps} replay {k}: loss {out['loss'].item():.6f}")
+        assert torch.equal(out["loss"], ref["loss"]), f"replay {k}: loss"
+        assert torch.equal(out["loss_rows"], ref["loss_rows"]), f"replay {k}: loss rows"
+        assert torch.equal(out["n_valid"], ref["n_valid"]), f"replay {k}: n_valid"
+        assert torch.equal(out["grad"].view(torch.int16), ref["grad"].view(torch.int16)), \
+            f"replay {k}: gradient"
