@@ -126,3 +126,37 @@ def test_mid_workload_full_size():
     P.assert_loss_rows(out["loss_rows"], ref, "mid full size")
     P.assert_scalar_loss(out["loss"].item(), ref["loss"], "mid full size")
     P.assert_grad_close(out["grad"], ref["grad"], "mid full size grad")
+
+
+def test_beyond_2_31_elements():
+    """T = 17000 rows of V = 128256 bf16 logits: 2.18e9 elements, so the
+    last rows start beyond 2^31 elements (and 2^32 bytes) of the logits and
+    of the gradient.  The fused call and the separate forward / backward
+    calls are checked on rows at both ends against the oracle; the batch
+    loss is the mean of the per-row losses."""
+    c = S.scaled(S.PAGE, 17000, 128256, 1011)
+    print(f"[full] T={c.T} V={c.V}: {c.T * c.V / 2 ** 31:.3f} x 2^31 elements", flush=True)
+    logits, target = S.generate(c, device=DEV, block_rows=2048)
+    T, V = logits.shape
+    first_far = (2 ** 31 + V - 1) // V          # first row starting beyond 2^31 elements
+    rows = np.array([0, 1, 2, T // 2, first_far - 1, first_far, first_far + 1, T - 3, T - 2,
+                     T - 1])
+    idx = torch.from_numpy(rows).to(DEV)
+    t = target.cpu().numpy()
+    n_valid = int((t != -100).sum())
+    out = vce.fused_fwd_bwd(logits, target)
+    torch.cuda.synchronize()
+    ref = P.oracle_for(logits[idx], target[idx], n_valid=n_valid)
+    P.assert_loss_rows(out["loss_rows"][idx], ref, "beyond 2^31: fused")
+    P.assert_grad_close(out["grad"][idx], ref["grad"], "beyond 2^31: fused grad")
+    lr = out["loss_rows"].double().cpu().numpy()
+    assert out["n_valid"].item() == n_valid
+    assert abs(out["loss"].item() - lr.sum() / n_valid) <= 1e-6 * abs(out["loss"].item())
+    grad = out["grad"]
+    del out
+    print("[full] forward, then backward", flush=True)
+    f = vce.forward(logits, target)
+    vce.backward(logits, target, f["fin"], f["n_valid"], grad=grad)
+    torch.cuda.synchronize()
+    P.assert_loss_rows(f["loss_rows"][idx], ref, "beyond 2^31: forward")
+    P.assert_grad_close(grad[idx], ref["grad"], "beyond 2^31: backward grad")

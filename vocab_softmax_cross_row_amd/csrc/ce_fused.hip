@@ -88,7 +88,7 @@ __device__ __forceinline__ double tab_exp8_slow(const u32x4 &w, const double *ta
 template <int IN, int OUT, int THREADS, int NV, bool LS, bool TAB>
 __device__ __forceinline__ void fused_row(const FusedArgs &a, int64_t row,
                                           BlockRed<THREADS> &red, GradConst &gc_sh,
-                                          const double *tab) {
+                                          double *tab) {
     using In = Elem<IN>;
     constexpr int EPV = In::kVec;
     using Ch = Chunk<IN, EPV>;
@@ -150,7 +150,7 @@ __device__ __forceinline__ void fused_row(const FusedArgs &a, int64_t row,
         const __amdgpu_buffer_rsrc_t rt =
             __builtin_amdgcn_make_buffer_rsrc((void *)a.exp_tab, 0, kExpTabN * 8, 0x00020000);
         const int wave_base = __builtin_amdgcn_readfirstlane((tid / kWave) * kWave);
-        u32x4 *tv = reinterpret_cast<u32x4 *>(const_cast<double *>(tab));
+        u32x4 *tv = reinterpret_cast<u32x4 *>(tab);
 #pragma unroll 1
         for (int q = 0; q * THREADS < kTabVecs; ++q)
             if (q * THREADS + tid < kTabVecs)
@@ -360,7 +360,7 @@ void k_fused_resident_tab(FusedArgs a) {
     __shared__ GradConst gc_sh;
     __shared__ u32x4 tab[(kExpTabN * 8 + 15) / 16];
     fused_row<CE_BF16, OUT, kTabThreads, NV, true, true>(a, xcd_major(blockIdx.x, gridDim.x), red,
-                                                         gc_sh, reinterpret_cast<const double *>(tab));
+                                                         gc_sh, reinterpret_cast<double *>(tab));
 }
 
 // ===========================================================================
