@@ -597,44 +597,72 @@ void k_fused_lds(FusedArgs a) {
 // ===========================================================================
 namespace vce {
 
-// (threads, vectors per thread) of the row-resident kernel, smallest first
+// (threads, vectors per thread) of the row-resident kernel, smallest first.
+// Short rows take small workgroups: a 256-thread workgroup per 1000-column
+// row left half of its threads idle (65536 x 1000 bf16: 157 us at 256 x 1,
+// 85 us at 64 x 2).  With smoothing the fp64 work per logit makes 64-thread
+// workgroups pay up to 4096 columns (65536 x 4096: 381 -> 333 us); without
+// it 256 x 2 stays best there (204 against 215 us).
 struct ResidentShape {
     int threads, nv;
 };
-constexpr ResidentShape kResident[] = {{256, 1}, {256, 2},  {256, 4},  {256, 8},
-                                       {256, 16}, {512, 16}, {1024, 16}};
+constexpr ResidentShape kResident[] = {{64, 1},   {64, 2},   {128, 2},   {256, 2}, {256, 4},
+                                       {256, 8},  {256, 16}, {512, 16},  {1024, 16}};
+constexpr ResidentShape kResidentLS[] = {{64, 1},  {64, 2},   {64, 4},    {64, 8},  {256, 4},
+                                         {256, 8}, {256, 16}, {512, 16},  {1024, 16}};
+constexpr int kNumResident = sizeof(kResident) / sizeof(kResident[0]);
+static_assert(kNumResident == sizeof(kResidentLS) / sizeof(kResidentLS[0]), "table sizes");
 
-static int resident_index(int in_dt, int64_t V) {
+static const ResidentShape *resident_table(bool ls) { return ls ? kResidentLS : kResident; }
+
+static int resident_index(int in_dt, int64_t V, bool ls) {
+    const ResidentShape *tab = resident_table(ls);
     const int64_t epv = (in_dt == CE_BF16) ? 8 : 4;
     const int64_t nvec = V / epv;
-    for (int i = 0; i < (int)(sizeof(kResident) / sizeof(kResident[0])); ++i)
-        if ((int64_t)kResident[i].threads * kResident[i].nv >= nvec &&
-            kResident[i].threads >= V - nvec * epv)
+    for (int i = 0; i < kNumResident; ++i)
+        if ((int64_t)tab[i].threads * tab[i].nv >= nvec && tab[i].threads >= V - nvec * epv)
             return i;
     return -1;
 }
 
 int resident_threads(int in_dt, int64_t V) {
-    const int i = resident_index(in_dt, V);
+    const int i = resident_index(in_dt, V, false);
     return i < 0 ? 0 : kResident[i].threads;
 }
 
 template <int IN, int OUT, bool LS>
 static hipError_t fused_dispatch(const FusedArgs &a, int64_t T, hipStream_t stream) {
-    const int i = resident_index(IN, a.V);
+    const int i = resident_index(IN, a.V, LS);
     const dim3 grid((unsigned)T);
 #define VCE_RES(TH, NV)                                                                         \
     hipLaunchKernelGGL((k_fused_resident<IN, OUT, TH, NV, LS>), grid, dim3(TH), 0, stream, a); \
     break;
-    switch (i) {
-    case 0: VCE_RES(256, 1)
-    case 1: VCE_RES(256, 2)
-    case 2: VCE_RES(256, 4)
-    case 3: VCE_RES(256, 8)
-    case 4: VCE_RES(256, 16)
-    case 5: VCE_RES(512, 16)
-    case 6: VCE_RES(1024, 16)
-    default: return hipErrorInvalidValue;
+    if constexpr (LS) {
+        switch (i) {
+        case 0: VCE_RES(64, 1)
+        case 1: VCE_RES(64, 2)
+        case 2: VCE_RES(64, 4)
+        case 3: VCE_RES(64, 8)
+        case 4: VCE_RES(256, 4)
+        case 5: VCE_RES(256, 8)
+        case 6: VCE_RES(256, 16)
+        case 7: VCE_RES(512, 16)
+        case 8: VCE_RES(1024, 16)
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (i) {
+        case 0: VCE_RES(64, 1)
+        case 1: VCE_RES(64, 2)
+        case 2: VCE_RES(128, 2)
+        case 3: VCE_RES(256, 2)
+        case 4: VCE_RES(256, 4)
+        case 5: VCE_RES(256, 8)
+        case 6: VCE_RES(256, 16)
+        case 7: VCE_RES(512, 16)
+        case 8: VCE_RES(1024, 16)
+        default: return hipErrorInvalidValue;
+        }
     }
 #undef VCE_RES
     return hipGetLastError();
@@ -658,9 +686,9 @@ static int lds_split_bytes(int in_dt, int64_t V) {
 }
 
 bool fused_table(int in_dt, int64_t V) {
-    const int i = resident_index(in_dt, V);
-    return in_dt == CE_BF16 && i >= 0 && kResident[i].threads == kTabThreads &&
-           kResident[i].nv == 16;
+    const int i = resident_index(in_dt, V, true);
+    return in_dt == CE_BF16 && i >= 0 && kResidentLS[i].threads == kTabThreads &&
+           kResidentLS[i].nv == 16;
 }
 
 bool fused_fits(int in_dt, int64_t V, bool aligned, bool smoothing) {
