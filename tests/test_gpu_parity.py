@@ -687,3 +687,32 @@ def test_graph_replay_matches_eager(V, eps):
         assert torch.equal(out["n_valid"], ref["n_valid"]), f"replay {k}: n_valid"
         assert torch.equal(out["grad"].view(torch.int16), ref["grad"].view(torch.int16)), \
             f"replay {k}: gradient"
+
+
+# --------------------------------------------------------------------------
+# the autograd wrapper: forward and backward through the C ABI
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("reduction,eps", [("mean", 0.0), ("sum", 0.1), ("none", 0.0)])
+def test_autograd_cross_entropy(reduction, eps):
+    """vce.cross_entropy under torch autograd: the loss of ce_forward, and a
+    gradient from ce_backward with the incoming gradient as grad_output
+    (3 x the loss, or per-row weights for reduction none)."""
+    c, logits, target = _case(S.PAGE, 400, 50257, 171, eps=eps)
+    x = logits.clone().requires_grad_(True)
+    loss = vce.cross_entropy(x, target, label_smoothing=eps, reduction=reduction)
+    if reduction == "none":
+        w = torch.linspace(-1.0, 2.0, c.T, device=DEV)
+        (loss * w).sum().backward()
+        go = w
+    else:
+        (3.0 * loss).backward()
+        go = 3.0
+    torch.cuda.synchronize()
+    ref = P.oracle_for(logits, target, eps=eps, reduction=reduction, grad_output=go)
+    if reduction == "none":
+        P.assert_loss_rows(loss.detach(), ref, f"autograd {reduction}")
+    else:
+        P.assert_scalar_loss(loss.item(), ref["loss"], f"autograd {reduction}")
+    assert x.grad.dtype == logits.dtype
+    P.assert_grad_close(x.grad, ref["grad"], f"autograd {reduction} grad")
