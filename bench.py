@@ -130,9 +130,9 @@ def main():
                     help="also run a plain copy of known size (for counter scaling)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the split-vocabulary "
-              "path shows one GPU's shard, and no multi-GPU run is part of this build",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library has no "
+              "collectives; the split-vocabulary measurement shows one GPU's shard of a "
+              "vocabulary-parallel step", file=sys.stderr)
         sys.exit(2)
 
     import torch
