@@ -570,8 +570,16 @@ int ce_linear_fwd_bwd(const ce_linear_problem *prob, const void *E, const void *
     }
     uint16_t *Ef = at<uint16_t>(ws, l.Ef), *Cf = at<uint16_t>(ws, l.Cf);
     const uint16_t *Eh = static_cast<const uint16_t *>(E), *Ch = static_cast<const uint16_t *>(C);
-    VCE_TRY(launch_relayout(RelayoutArgs{Eh, N, D, D, Ef, l.Np, l.Dp}, false, s));
-    VCE_TRY(launch_relayout(RelayoutArgs{Ch, V, D, D, Cf, l.Vp, l.Dp}, false, s));
+    uint16_t *ETf = bwd ? at<uint16_t>(ws, l.ETf) : nullptr;
+    uint16_t *CTf = bwd ? at<uint16_t>(ws, l.CTf) : nullptr;
+    if (bwd) {
+        // both operand forms of E and of C from one read of each
+        VCE_TRY(launch_relayout(RelayoutArgs{Eh, N, D, D, ETf, l.Dr, l.Np}, true, s, Ef, l.Dp));
+        VCE_TRY(launch_relayout(RelayoutArgs{Ch, V, D, D, CTf, l.Dr, l.Vp}, true, s, Cf, l.Dp));
+    } else {
+        VCE_TRY(launch_relayout(RelayoutArgs{Eh, N, D, D, Ef, l.Np, l.Dp}, false, s));
+        VCE_TRY(launch_relayout(RelayoutArgs{Ch, V, D, D, Cf, l.Vp, l.Dp}, false, s));
+    }
 
     // forward: per (256-class tile, row) statistics of the logits, merged
     const bool ls = p.label_smoothing > 0.0f;
@@ -599,9 +607,6 @@ int ce_linear_fwd_bwd(const ce_linear_problem *prob, const void *E, const void *
     if (!bwd) return CE_OK;
 
     // backward: per class chunk, G and G^T (bf16), then dC rows and dE
-    uint16_t *ETf = at<uint16_t>(ws, l.ETf), *CTf = at<uint16_t>(ws, l.CTf);
-    VCE_TRY(launch_relayout(RelayoutArgs{Eh, N, D, D, ETf, l.Dr, l.Np}, true, s));
-    VCE_TRY(launch_relayout(RelayoutArgs{Ch, V, D, D, CTf, l.Dr, l.Vp}, true, s));
     void *rows = at<char>(ws, l.rows);
     LinRowArgs ra{fin, target, nv, grad_output, p.reduction, p.label_smoothing, N, V, rows};
     VCE_TRY(launch_linear_rowconst(ra, s));

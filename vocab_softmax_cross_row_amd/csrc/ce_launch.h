@@ -192,7 +192,10 @@ struct LinMergeArgs {
 };
 
 hipError_t launch_linear_merge(const LinMergeArgs &a, hipStream_t stream);
-hipError_t launch_relayout(const RelayoutArgs &a, bool transpose, hipStream_t stream);
+// transpose with Yn: also the plain fragment-major form of X into Yn (rows
+// padded to a.Kp, K padded to Kn, Kn <= a.Rp), from the same reads of X
+hipError_t launch_relayout(const RelayoutArgs &a, bool transpose, hipStream_t stream,
+                           uint16_t *Yn = nullptr, int64_t Kn = 0);
 hipError_t launch_linear_rowconst(const LinRowArgs &a, hipStream_t stream);
 hipError_t launch_gemm(const GemmArgs &g, int epi, bool ls, hipStream_t stream);
 hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t stream);

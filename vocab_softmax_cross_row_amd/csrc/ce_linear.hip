@@ -72,7 +72,11 @@ __global__ __launch_bounds__(kRelayoutThreads) void k_relayout(RelayoutArgs a) {
 // Transposed re-layout: Y = fragment-major form of X^T, padded to [Rp, Kp]
 // (Y's rows are X's columns, Y's K is X's rows).  A workgroup moves a
 // 64 x 64 tile through LDS: 16-byte row loads of X, 16-byte slot stores of Y.
-__global__ __launch_bounds__(kRelayoutThreads) void k_relayout_t(RelayoutArgs a) {
+// With Yn, the same loads also give the plain fragment-major form of X
+// (rows padded to Kp, K padded to Kn): each 16-byte row load is one of its
+// fragment slots, so X is read once for both forms.
+__global__ __launch_bounds__(kRelayoutThreads) void k_relayout_t(RelayoutArgs a, uint16_t *Yn,
+                                                                 int64_t Kn) {
     __shared__ uint16_t t[64][64 + 2];
     const int tid = threadIdx.x;
     const int64_t tiles_y = a.Rp / 64;                        // tiles along Y rows
@@ -86,6 +90,12 @@ __global__ __launch_bounds__(kRelayoutThreads) void k_relayout_t(RelayoutArgs a)
         const int64_t r = x0 + lr, c = y0 + lc;
         u32x4 v = {0u, 0u, 0u, 0u};
         if (r < a.R && c < a.K) v = *reinterpret_cast<const u32x4 *>(a.X + r * a.ld + c);
+        if (Yn && c < Kn) {
+            // lane (r % 32) + 32 ((c / 8) % 2) of block (r / 32, c / 16)
+            const int L = (int)(r & 31) + 32 * (int)((c >> 3) & 1);
+            *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(Yn) + frag_off(r >> 5, c >> 4, Kn) +
+                                       L * 16) = v;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             t[lr][lc + 2 * e] = (uint16_t)(v[e] & 0xffffu);
@@ -697,14 +707,15 @@ hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_relayout(const RelayoutArgs &a, bool transpose, hipStream_t stream) {
+hipError_t launch_relayout(const RelayoutArgs &a, bool transpose, hipStream_t stream,
+                           uint16_t *Yn, int64_t Kn) {
     if (!transpose) {
         const int64_t slots = a.Rp * a.Kp / 8;
         const dim3 grid((unsigned)((slots + kRelayoutThreads - 1) / kRelayoutThreads));
         hipLaunchKernelGGL(k_relayout, grid, dim3(kRelayoutThreads), 0, stream, a);
     } else {
         const dim3 grid((unsigned)((a.Rp / 64) * (a.Kp / 64)));
-        hipLaunchKernelGGL(k_relayout_t, grid, dim3(kRelayoutThreads), 0, stream, a);
+        hipLaunchKernelGGL(k_relayout_t, grid, dim3(kRelayoutThreads), 0, stream, a, Yn, Kn);
     }
     return hipGetLastError();
 }
