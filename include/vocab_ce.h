@@ -237,7 +237,7 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
  * of a chunk are complete after it, dE is summed over the chunks in fp32 or,
  * with CE_ACC_KAHAN, with a Kahan compensation term (one more [N, D] fp32
  * workspace buffer).  Everything is deterministic (no atomics). */
-#define CE_LINEAR_CHUNK 8192
+#define CE_LINEAR_CHUNK 16384
 
 typedef enum {
     CE_ACC_FP32 = 0, /* dE summed over vocabulary chunks in fp32 */

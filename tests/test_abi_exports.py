@@ -84,6 +84,15 @@ def test_null_and_dtype_checks(lib):
                           None, 0, None) == -10
 
 
+def test_header_constants_match_the_binding():
+    """The binding's copies of the header's #define constants."""
+    hdr = open(os.path.join(ROOT, "include", "vocab_ce.h")).read()
+    for name in ("CE_LINEAR_CHUNK", "CE_MAX_SHARDS"):
+        m = re.search(r"#define\s+" + name + r"\s+(\d+)", hdr)
+        assert m, name
+        assert int(m.group(1)) == getattr(B, name), name
+
+
 def test_linear_problem_struct_and_workspace(lib):
     assert ctypes.sizeof(B.CELinearProblem) == 48
     p = B.make_linear_problem(8192, 2048, 128256)

@@ -19,6 +19,7 @@ import pytest
 import torch
 
 import vocab_softmax_cross_row_amd as vce
+from vocab_softmax_cross_row_amd import _binding as B
 from synth import ce_inputs as S
 from tests.parity_util import (LOSS_RTOL, assert_linear_grad_close, assert_loss_rows,
                                assert_scalar_loss, linear_oracle_for)
@@ -71,7 +72,7 @@ def test_ragged_in_every_dimension():
 @pytest.mark.parametrize("accum", ["fp32", "kahan"])
 def test_several_chunks_with_smoothing(accum):
     # 2 vocabulary chunks, the second ragged; sum with a grad_output of 0.5
-    case = _case(512, 256, 8192 + 300, 2102, eps=0.1, reduction="sum")
+    case = _case(512, 256, B.CE_LINEAR_CHUNK + 300, 2102, eps=0.1, reduction="sum")
     go = torch.tensor([0.5], device=DEV)
     E, C, t, out = _run(case, accum=accum, grad_output=go)
     _check(case, E, C, t, out, grad_output=go, what=f"chunks {accum}")
@@ -92,7 +93,7 @@ def test_cce_issue_toy_shape():
 
 
 def test_kahan_and_fp32_agree_closely():
-    case = _case(256, 128, 3 * 8192, 2104)
+    case = _case(256, 128, 3 * B.CE_LINEAR_CHUNK, 2104)
     E, C, t, a = _run(case, accum="fp32")
     b = vce.linear_cross_entropy(E, C, t, accum="kahan")
     torch.cuda.synchronize()

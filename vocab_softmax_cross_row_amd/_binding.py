@@ -31,7 +31,7 @@ EXPORTS = ("ce_workspace_bytes", "ce_forward", "ce_merge_shard_stats", "ce_backw
            "ce_status_str", "ce_version")
 CE_ACC_FP32, CE_ACC_KAHAN = 0, 1
 ACCUMS = {"fp32": CE_ACC_FP32, "kahan": CE_ACC_KAHAN}
-CE_LINEAR_CHUNK = 8192
+CE_LINEAR_CHUNK = 16384
 
 # device structs, as numpy dtypes for reading them back
 ROW_STATS_DTYPE = np.dtype([("m", "<f4"), ("zt", "<f4"), ("own", "<i4"), ("reserved", "<i4"),
