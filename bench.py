@@ -12,8 +12,10 @@ fixed seed before timing and stay in HBM.  Prints one JSON line.
 
 Extra objects in the line:
   roofline      HBM roofline of the fused kernel: algorithmic bytes of one
-                launch / the average step time from HIP events on the launch
-                stream; peak 8 TB/s.  traffic is the HBM byte count the
+                launch / its average duration, from HIP events the library
+                records around it on the launch stream (ce_set_fused_events;
+                the step also holds the target count and the loss reduction,
+                about 12 us); peak 8 TB/s.  traffic is the HBM byte count the
                 rocprofv3 FETCH_SIZE / WRITE_SIZE counters gave for this
                 kernel source (profiles/fused_page_counters.md), or null if
                 the kernel source changed since.
@@ -177,6 +179,26 @@ def main():
     print(f"# fused: {ms:.4f} ms/step (events), {wall / args.steps * 1e3:.4f} ms/step (wall), "
           f"loss {loss.item():.6f}, n_valid {n_valid.item()}", file=sys.stderr, flush=True)
 
+    # the fused kernel alone: the library records a pair of HIP events on the
+    # launch stream around the step's main kernel (ce_set_fused_events), one
+    # pair per step, over another K steps
+    pairs = []
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    for a, b in pairs:
+        B.ce_set_fused_events(a.cuda_event, b.cuda_event)
+        step()
+    B.ce_set_fused_events(None, None)
+    torch.cuda.synchronize()
+    kms = sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+    kgbs = fused_bytes(T, V) / (kms * 1e-3) / 1e9
+    print(f"# fused kernel alone: {kms * 1e3:.1f} us per launch (events around it)",
+          file=sys.stderr, flush=True)
+
     split = None
     if not args.no_split:
         half = V // 2
@@ -331,9 +353,10 @@ def main():
                    "T": T, "V": V, "logits_dtype": "bf16", "grad_dtype": "bf16",
                    "reduction": "mean", "ignored_rows": case.n_ignored,
                    "confident_rows": case.n_margin, "logits": "N(0, 3^2), seed 1003"},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "traffic": counter_traffic(), "algorithmic_bytes": nbytes},
+        "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
+                     "traffic": counter_traffic(), "algorithmic_bytes": nbytes,
+                     "kernel": "k_fused_lds", "kernel_us": round(kms * 1e3, 1)},
         "cpu_baseline": cpu,
         "split_v": split,
         "unfused": unfused,

@@ -283,6 +283,17 @@ const char *ce_status_str(int status);
 /* Library version as MAJOR * 10000 + MINOR * 100 + PATCH.  Host function. */
 int ce_version(void);
 
+/* Measurement hook (host function; the setting belongs to the calling host
+ * thread).  With both events set (hipEvent_t handles created by the caller,
+ * passed as void *), every later ce_fused_fwd_bwd on this thread records
+ * `start` on its stream just before its main kernels (everything after the
+ * count of valid targets and before the loss reduction) and `stop` just
+ * after them, so that the caller can time the fused kernel alone with
+ * hipEventElapsedTime.  ce_set_fused_events(NULL, NULL), the default, turns
+ * it off.  Returns CE_ERR_ARG if exactly one event is NULL.  The events stay
+ * owned by the caller and must outlive the calls that record them. */
+int ce_set_fused_events(void *start, void *stop);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,6 +52,10 @@ def test_host_only_calls(lib):
     assert B.ce_workspace_bytes(small, B.CE_OP_FUSED) >= 8 * 32 * 2
     bad = B.make_problem(4, 10, label_smoothing=1.5)
     assert B.ce_workspace_bytes(bad, B.CE_OP_FUSED) == 0
+    # the measurement hook takes both events or neither (host-side setting)
+    assert lib.ce_set_fused_events(ctypes.c_void_p(16), None) == -10
+    assert lib.ce_set_fused_events(None, ctypes.c_void_p(16)) == -10
+    assert lib.ce_set_fused_events(None, None) == 0
 
 
 @pytest.mark.parametrize("kw,status", [

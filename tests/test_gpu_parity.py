@@ -716,3 +716,29 @@ def test_autograd_cross_entropy(reduction, eps):
         P.assert_scalar_loss(loss.item(), ref["loss"], f"autograd {reduction}")
     assert x.grad.dtype == logits.dtype
     P.assert_grad_close(x.grad, ref["grad"], f"autograd {reduction} grad")
+
+
+def test_fused_events_bracket_the_kernel():
+    """ce_set_fused_events: the events recorded around the fused call's main
+    kernel time it (a positive duration below the whole call's), and the
+    call's results are those of a call without them."""
+    c, logits, target = _case(S.PAGE, 600, 128256, 181)
+    ref = vce.fused_fwd_bwd(logits, target)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    b.record()
+    torch.cuda.synchronize()
+    vce.ce_set_fused_events(a.cuda_event, b.cuda_event)
+    try:
+        w0.record()
+        out = vce.fused_fwd_bwd(logits, target)
+        w1.record()
+    finally:
+        vce.ce_set_fused_events(None, None)
+    torch.cuda.synchronize()
+    k, whole = a.elapsed_time(b), w0.elapsed_time(w1)
+    _say(f"[events] fused kernel {k * 1e3:.1f} us of a {whole * 1e3:.1f} us call")
+    assert 0.0 < k < whole
+    assert torch.equal(out["loss"], ref["loss"])
+    assert torch.equal(out["grad"].view(torch.int16), ref["grad"].view(torch.int16))

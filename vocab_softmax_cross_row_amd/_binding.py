@@ -28,7 +28,7 @@ REDUCTIONS = {"none": CE_RED_NONE, "sum": CE_RED_SUM, "mean": CE_RED_MEAN}
 # symbols declared in include/vocab_ce.h
 EXPORTS = ("ce_workspace_bytes", "ce_forward", "ce_merge_shard_stats", "ce_backward",
            "ce_fused_fwd_bwd", "ce_linear_workspace_bytes", "ce_linear_fwd_bwd",
-           "ce_status_str", "ce_version")
+           "ce_status_str", "ce_version", "ce_set_fused_events")
 CE_ACC_FP32, CE_ACC_KAHAN = 0, 1
 ACCUMS = {"fp32": CE_ACC_FP32, "kahan": CE_ACC_KAHAN}
 CE_LINEAR_CHUNK = 16384
@@ -94,6 +94,8 @@ def lib():
         L.ce_status_str.restype = ctypes.c_char_p
         L.ce_version.argtypes = []
         L.ce_version.restype = i32
+        L.ce_set_fused_events.argtypes = [P, P]
+        L.ce_set_fused_events.restype = i32
         _lib = L
     return _lib
 
@@ -197,6 +199,13 @@ def ce_status_str(status):
 
 def ce_version():
     return int(lib().ce_version())
+
+
+def ce_set_fused_events(start, stop):
+    """Events (raw hipEvent_t handles, or None) recorded around the main
+    kernels of later ce_fused_fwd_bwd calls on this host thread."""
+    _check("ce_set_fused_events", lib().ce_set_fused_events(
+        ctypes.c_void_p(start) if start else None, ctypes.c_void_p(stop) if stop else None))
 
 
 def read_stats(raw):

@@ -33,6 +33,10 @@ constexpr int64_t kSmoothedResidentMaxCols = 32768;
 
 constexpr size_t kAlign = 256;
 
+// ce_set_fused_events: events recorded around the fused call's main
+// kernels, per host thread (NULL: off)
+thread_local hipEvent_t g_fused_start = nullptr, g_fused_stop = nullptr;
+
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
@@ -437,6 +441,7 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
     VCE_TRY(launch_count(target, p.T, p.ignore_index, p.V_total, nv, err_count, s));
     float *lr = loss_rows ? loss_rows : at<float>(ws, l.loss_rows);
 
+    if (p.T > 0 && g_fused_start) VCE_TRY(hipEventRecord(g_fused_start, s));
     if (p.T > 0) {
         const bool vec = vec_ok(logits, p.ld, logits_dtype, grad, ldg, grad_dtype);
         const bool svec = stream_vec_ok(logits, p.ld, logits_dtype, grad, ldg, grad_dtype);
@@ -523,6 +528,7 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
             VCE_TRY(launch_grad(ga, logits_dtype, grad_dtype, svec, p.T, s));
         }
     }
+    if (p.T > 0 && g_fused_stop) VCE_TRY(hipEventRecord(g_fused_stop, s));
     if (loss && p.reduction != CE_RED_NONE)
         VCE_TRY(launch_reduce(lr, p.T, p.reduction, nv, loss, s));
     return CE_OK;
@@ -682,5 +688,12 @@ const char *ce_status_str(int status) {
 }
 
 int ce_version(void) { return 100; }
+
+int ce_set_fused_events(void *start, void *stop) {
+    if ((start == nullptr) != (stop == nullptr)) return CE_ERR_ARG;
+    g_fused_start = static_cast<hipEvent_t>(start);
+    g_fused_stop = static_cast<hipEvent_t>(stop);
+    return CE_OK;
+}
 
 } // extern "C"
