@@ -742,3 +742,34 @@ def test_fused_events_bracket_the_kernel():
     assert 0.0 < k < whole
     assert torch.equal(out["loss"], ref["loss"])
     assert torch.equal(out["grad"].view(torch.int16), ref["grad"].view(torch.int16))
+
+
+@pytest.mark.parametrize("V,eps,out_dt", [(70001, 0.1, torch.float32), (70001, 0.0, torch.bfloat16),
+                                          (100000, 0.2, torch.float32)])
+def test_fp32_rows_too_long_for_registers(V, eps, out_dt):
+    """fp32 logits longer than the register-resident kernels hold (65536
+    columns) stream: column-chunk statistics (fp64 online sums with
+    smoothing), the on-device merge, the gradient pass; odd widths peel
+    each row's head."""
+    c, logits, target = _case(S.TINY, 300, V, 191 + V % 7, eps=eps)
+    target[0] = V - 1
+    _fused_check(c, logits, target, grad_dtype=out_dt, what=f"fp32 long rows V={V} eps={eps}")
+
+
+def test_fp32_shards_with_smoothing():
+    """fp32 logits as three vocabulary shards of unequal width with
+    smoothing: per-shard statistics, merge, per-shard backward."""
+    c, logits, target = _case(S.TINY, 500, 30000, 197, eps=0.1)
+    V = c.V
+    edges = [0, 7001, 20000, V]
+    stats = [vce.forward(logits[:, a:b], target, vocab_start=a, V_total=V,
+                         label_smoothing=0.1)["stats"] for a, b in zip(edges[:-1], edges[1:])]
+    m = vce.merge_shard_stats(stats, target, V, label_smoothing=0.1)
+    grads = [vce.backward(logits[:, a:b], target, m["fin"], m["n_valid"], vocab_start=a,
+                          V_total=V, label_smoothing=0.1) for a, b in zip(edges[:-1], edges[1:])]
+    torch.cuda.synchronize()
+    ref = P.oracle_for(logits, target, eps=0.1)
+    P.assert_loss_rows(m["loss_rows"], ref, "fp32 shards")
+    P.assert_scalar_loss(m["loss"].item(), ref["loss"], "fp32 shards")
+    for (a, b), g in zip(zip(edges[:-1], edges[1:]), grads):
+        P.assert_grad_close(g, ref["grad"][:, a:b], f"fp32 shard [{a},{b})")
