@@ -773,3 +773,38 @@ def test_fp32_shards_with_smoothing():
     P.assert_scalar_loss(m["loss"].item(), ref["loss"], "fp32 shards")
     for (a, b), g in zip(zip(edges[:-1], edges[1:]), grads):
         P.assert_grad_close(g, ref["grad"][:, a:b], f"fp32 shard [{a},{b})")
+
+
+def test_ignore_index_inside_the_vocabulary_and_per_row_grad_output_on_shards():
+    """ignore_index is a parameter and may be a class id (7 here): rows whose
+    target is 7 are ignored on every path.  With reduction none, the shard
+    backward scales row r by grad_output[r]."""
+    c, logits, target = _case(S.PAGE, 640, 50000, 199, eps=0.1)
+    target[target == -100] = 11  # -100 would be a bad target once 7 is the ignore index
+    target[::9] = 7
+    t = target.cpu().numpy()
+    go = torch.linspace(-1.5, 2.5, c.T, device=DEV)
+    # fused, mean
+    out = vce.fused_fwd_bwd(logits, target, ignore_index=7, label_smoothing=0.1)
+    torch.cuda.synchronize()
+    ref = P.oracle_for(logits, target, ignore_index=7, eps=0.1)
+    assert int(out["n_valid"].item()) == ref["n_valid"] == int((t != 7).sum())
+    P.assert_loss_rows(out["loss_rows"], ref, "ignore 7 fused")
+    P.assert_grad_close(out["grad"], ref["grad"], "ignore 7 fused grad")
+    assert torch.all(out["grad"].cpu()[torch.from_numpy(t == 7)] == 0)
+    # two shards, reduction none with a per-row grad_output
+    V, h = c.V, 23456
+    stats = [vce.forward(logits[:, a:b], target, vocab_start=a, V_total=V, ignore_index=7,
+                         label_smoothing=0.1, reduction="none")["stats"]
+             for a, b in ((0, h), (h, V))]
+    m = vce.merge_shard_stats(stats, target, V, ignore_index=7, label_smoothing=0.1,
+                              reduction="none")
+    grads = [vce.backward(logits[:, a:b], target, m["fin"], m["n_valid"], grad_output=go,
+                          vocab_start=a, V_total=V, ignore_index=7, label_smoothing=0.1,
+                          reduction="none") for a, b in ((0, h), (h, V))]
+    torch.cuda.synchronize()
+    ref = P.oracle_for(logits, target, ignore_index=7, eps=0.1, reduction="none",
+                       grad_output=go)
+    P.assert_loss_rows(m["loss_rows"], ref, "ignore 7 shards")
+    P.assert_grad_close(grads[0], ref["grad"][:, :h], "ignore 7 shard 0")
+    P.assert_grad_close(grads[1], ref["grad"][:, h:], "ignore 7 shard 1")
