@@ -808,3 +808,21 @@ def test_ignore_index_inside_the_vocabulary_and_per_row_grad_output_on_shards():
     P.assert_loss_rows(m["loss_rows"], ref, "ignore 7 shards")
     P.assert_grad_close(grads[0], ref["grad"][:, :h], "ignore 7 shard 0")
     P.assert_grad_close(grads[1], ref["grad"][:, h:], "ignore 7 shard 1")
+
+
+@pytest.mark.parametrize("V,dt,eps", [(128256, "bf16", 0.0), (128256, "bf16", 0.1),
+                                      (1000, "f32", 0.0), (2, "bf16", 0.1), (40001, "f32", 0.1)])
+def test_single_row(V, dt, eps):
+    """One row (T = 1): the split-V grid for long rows, the resident kernel
+    for short ones, and the smallest vocabulary with a real softmax."""
+    base = S.PAGE if dt == "bf16" else S.TINY
+    c, logits, target = _case(base, 1, V, 211 + V % 5, eps=eps)
+    if int(target[0]) == -100:
+        target[0] = V - 1
+    _fused_check(c, logits, target, what=f"T=1 V={V} {dt} eps={eps}")
+    f = vce.forward(logits, target, label_smoothing=eps)
+    g = vce.backward(logits, target, f["fin"], f["n_valid"], label_smoothing=eps)
+    torch.cuda.synchronize()
+    ref = P.oracle_for(logits, target, eps=eps)
+    P.assert_loss_rows(f["loss_rows"], ref, "T=1 unfused")
+    P.assert_grad_close(g, ref["grad"], "T=1 unfused grad")
