@@ -78,6 +78,15 @@ def test_several_chunks_with_smoothing(accum):
     _check(case, E, C, t, out, grad_output=go, what=f"chunks {accum}")
 
 
+@pytest.mark.parametrize("accum", ["fp32", "kahan"])
+def test_mean_with_smoothing_over_two_chunks(accum):
+    # mean over the non-ignored rows with smoothing; the vocabulary spans one
+    # full backward chunk and a ragged second one
+    case = _case(300, 128, B.CE_LINEAR_CHUNK + 3616, 2105, eps=0.1)
+    E, C, t, out = _run(case, accum=accum)
+    _check(case, E, C, t, out, what=f"mean smoothing {accum}")
+
+
 def test_reduction_none_per_row_grad_output():
     case = _case(260, 64, 700, 2103, reduction="none")
     go = torch.linspace(0.25, 2.0, 260, device=DEV)
