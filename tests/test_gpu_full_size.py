@@ -82,6 +82,32 @@ def test_fused_full_size(page):
     P.assert_scalar_loss(out["loss"].item(), loss, "full-size loss")
 
 
+def test_fused_full_size_every_element(page):
+    """Every per-row loss and every one of the 2.1e9 gradient elements of
+    the page-scale fused call against the oracle, in blocks of 1024 rows
+    (the oracle's gradient of a block is 1 GB of fp64)."""
+    logits, target = page
+    T, V = logits.shape
+    out = vce.fused_fwd_bwd(logits, target)
+    torch.cuda.synchronize()
+    t = target.cpu().numpy()
+    n_valid = int((t != -100).sum())
+    worst, ones = 0, 0
+    for r0 in range(0, T, 1024):
+        r1 = min(T, r0 + 1024)
+        ref = P.oracle_for(logits[r0:r1], target[r0:r1], n_valid=n_valid)
+        P.assert_loss_rows(out["loss_rows"][r0:r1], ref, f"rows [{r0},{r1})")
+        g = P.ordered_bf16(P.bf16_bits(out["grad"][r0:r1]))
+        d = np.abs(g - P.ordered_bf16(O.to_bf16(ref["grad"])))
+        worst = max(worst, int(d.max()))
+        ones += int((d == 1).sum())
+        assert worst <= P.BF16_ULPS, f"rows [{r0},{r1}): bf16 gradient off by {worst} ulp"
+        if r0 % 4096 == 0:
+            print(f"[full] every element: rows [0,{r1}) checked, max {worst} ulp", flush=True)
+    print(f"[full] every element: {T * V} gradients, max {worst} ulp, {ones} at 1 ulp",
+          flush=True)
+
+
 def test_split_vocabulary_full_size(page):
     logits, target = page
     T, V = logits.shape
