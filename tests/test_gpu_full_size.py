@@ -186,3 +186,38 @@ def test_beyond_2_31_elements():
     torch.cuda.synchronize()
     P.assert_loss_rows(f["loss_rows"][idx], ref, "beyond 2^31: forward")
     P.assert_grad_close(grad[idx], ref["grad"], "beyond 2^31: backward grad")
+
+
+def test_split_vocabulary_full_size_every_element(page):
+    """The split-vocabulary step with smoothing 0.1 (two 64128-column shards,
+    merge, per-shard backward): every per-row loss and every gradient
+    element against the oracle over the whole vocabulary, in row blocks."""
+    logits, target = page
+    T, V = logits.shape
+    half, eps = V // 2, 0.1
+    s1 = vce.forward(logits[:, :half], target, vocab_start=0, V_total=V, label_smoothing=eps)
+    s2 = vce.forward(logits[:, half:], target, vocab_start=half, V_total=V,
+                     label_smoothing=eps)
+    m = vce.merge_shard_stats([s1["stats"], s2["stats"]], target, V, label_smoothing=eps)
+    grad = torch.empty_like(logits)
+    vce.backward(logits[:, :half], target, m["fin"], m["n_valid"], vocab_start=0, V_total=V,
+                 label_smoothing=eps, grad=grad[:, :half])
+    vce.backward(logits[:, half:], target, m["fin"], m["n_valid"], vocab_start=half,
+                 V_total=V, label_smoothing=eps, grad=grad[:, half:])
+    torch.cuda.synchronize()
+    t = target.cpu().numpy()
+    n_valid = int((t != -100).sum())
+    worst, ones = 0, 0
+    for r0 in range(0, T, 1024):
+        r1 = min(T, r0 + 1024)
+        ref = P.oracle_for(logits[r0:r1], target[r0:r1], eps=eps, n_valid=n_valid)
+        P.assert_loss_rows(m["loss_rows"][r0:r1], ref, f"shards rows [{r0},{r1})")
+        g = P.ordered_bf16(P.bf16_bits(grad[r0:r1]))
+        d = np.abs(g - P.ordered_bf16(O.to_bf16(ref["grad"])))
+        worst = max(worst, int(d.max()))
+        ones += int((d == 1).sum())
+        assert worst <= P.BF16_ULPS, f"shards rows [{r0},{r1}): off by {worst} ulp"
+        if r0 % 4096 == 0:
+            print(f"[full] shards, every element: rows [0,{r1}) checked", flush=True)
+    print(f"[full] shards, every element: {T * V} gradients, max {worst} ulp, {ones} at 1 ulp",
+          flush=True)
