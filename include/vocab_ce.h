@@ -283,16 +283,22 @@ const char *ce_status_str(int status);
 /* Library version as MAJOR * 10000 + MINOR * 100 + PATCH.  Host function. */
 int ce_version(void);
 
-/* Measurement hook (host function; the setting belongs to the calling host
- * thread).  With both events set (hipEvent_t handles created by the caller,
- * passed as void *), every later ce_fused_fwd_bwd on this thread records
- * `start` on its stream just before its main kernels (everything after the
- * count of valid targets and before the loss reduction) and `stop` just
- * after them, so that the caller can time the fused kernel alone with
- * hipEventElapsedTime.  ce_set_fused_events(NULL, NULL), the default, turns
- * it off.  Returns CE_ERR_ARG if exactly one event is NULL.  The events stay
- * owned by the caller and must outlive the calls that record them. */
-int ce_set_fused_events(void *start, void *stop);
+/* ======================================================================== */
+/* MEASUREMENT ONLY -- not part of the computation.                          */
+/* ======================================================================== */
+
+/* ce_fused_fwd_bwd, plus two HIP events (hipEvent_t handles created and
+ * owned by the caller, passed as void *) recorded on `stream`: ev_start just
+ * before the call's main kernels (after the count of valid targets) and
+ * ev_stop just after them (before the loss reduction), so that a benchmark
+ * can time the fused kernel alone with hipEventElapsedTime.  Both NULL: the
+ * same as ce_fused_fwd_bwd.  CE_ERR_ARG if exactly one is NULL.  Results
+ * are bit-identical to ce_fused_fwd_bwd; the library keeps no state. */
+int ce_fused_fwd_bwd_timed(const ce_problem *prob, const void *logits, int logits_dtype,
+                           const int64_t *target, const float *grad_output, float *loss_rows,
+                           float *loss, int32_t *n_valid, int32_t *err_count, void *grad,
+                           int grad_dtype, int64_t ldg, void *ws, size_t ws_bytes, void *stream,
+                           void *ev_start, void *ev_stop);
 
 #ifdef __cplusplus
 }

@@ -468,12 +468,27 @@ void oracle_linear_backward(const void *E, const void *C, int dtype, int64_t n, 
     }
     if (!dC && !rsC)
         return;
+    /* dC[v, d] = sum over r = 0, 1, ..., n-1 of G[r, v] E[r, d].  Column v of G
+     * and column d of E are first copied out contiguously, so the sum walks
+     * memory in order; the terms and their order are those of the definition. */
+    double *GT = (double *)malloc((size_t)V * (size_t)n * sizeof(double));
+    double *ET = (double *)malloc((size_t)D * (size_t)n * sizeof(double));
+#pragma omp parallel for schedule(static)
+    for (int64_t v = 0; v < V; ++v)
+        for (int64_t r = 0; r < n; ++r)
+            GT[(size_t)v * (size_t)n + r] = G[(size_t)r * (size_t)V + v];
+#pragma omp parallel for schedule(static)
+    for (int64_t d = 0; d < D; ++d)
+        for (int64_t r = 0; r < n; ++r)
+            ET[(size_t)d * (size_t)n + r] = load_elem(E, dtype, r * D + d);
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t v = 0; v < V; ++v) {
+        const double *gv = GT + (size_t)v * (size_t)n;
         for (int64_t d = 0; d < D; ++d) {
+            const double *ed = ET + (size_t)d * (size_t)n;
             double acc = 0.0, sq = 0.0;
             for (int64_t r = 0; r < n; ++r) {
-                const double p = G[(size_t)r * (size_t)V + v] * load_elem(E, dtype, r * D + d);
+                const double p = gv[r] * ed[r];
                 acc += p;
                 sq += p * p;
             }
@@ -481,6 +496,8 @@ void oracle_linear_backward(const void *E, const void *C, int dtype, int64_t n, 
             if (rsC) rsC[v * D + d] = sqrt(sq);
         }
     }
+    free(GT);
+    free(ET);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -529,5 +546,17 @@ int oracle_threads(void)
     return omp_get_max_threads();
 #else
     return 1;
+#endif
+}
+
+/* Sets the number of OpenMP threads later calls use (n >= 1); used to time
+ * the oracle on one host core.  No effect on any result. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
 #endif
 }

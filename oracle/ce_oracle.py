@@ -61,6 +61,8 @@ def _load():
         lib.oracle_linear_backward.restype = None
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = i
+        lib.oracle_set_threads.argtypes = [i]
+        lib.oracle_set_threads.restype = None
         _lib = lib
     return _lib
 
@@ -259,3 +261,8 @@ def bf16_to_f64(bits):
 def threads():
     """OpenMP threads the oracle's row loops use."""
     return int(_load().oracle_threads())
+
+
+def set_threads(n):
+    """OpenMP threads for later calls (timing only; results do not change)."""
+    _load().oracle_set_threads(int(n))

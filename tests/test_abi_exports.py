@@ -52,10 +52,13 @@ def test_host_only_calls(lib):
     assert B.ce_workspace_bytes(small, B.CE_OP_FUSED) >= 8 * 32 * 2
     bad = B.make_problem(4, 10, label_smoothing=1.5)
     assert B.ce_workspace_bytes(bad, B.CE_OP_FUSED) == 0
-    # the measurement hook takes both events or neither (host-side setting)
-    assert lib.ce_set_fused_events(ctypes.c_void_p(16), None) == -10
-    assert lib.ce_set_fused_events(None, ctypes.c_void_p(16)) == -10
-    assert lib.ce_set_fused_events(None, None) == 0
+    # the measurement entry point takes both events or neither (checked
+    # before anything else, so nothing is launched here)
+    nul = [None] * 9
+    for ev in ((ctypes.c_void_p(16), None), (None, ctypes.c_void_p(16))):
+        assert lib.ce_fused_fwd_bwd_timed(ctypes.byref(p), None, 1, None, None, None, None,
+                                          None, None, None, 1, 16, None, 0, None, *ev) == -10
+    del nul
 
 
 @pytest.mark.parametrize("kw,status", [

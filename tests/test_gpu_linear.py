@@ -8,8 +8,10 @@ backward products).  Shapes cover padding in every dimension (tokens not a
 multiple of 256, hidden size not a multiple of 64, classes not a multiple
 of 256), several vocabulary chunks with a ragged last one, both dE
 accumulation modes, label smoothing, every reduction, the toy shape of
-apple/ml-cross-entropy issue #14, and the full 8192 x 2048 x 128256
-workload (sampled rows; full gradients at 16 rows of the full width).
+apple/ml-cross-entropy issue #14, every element of dE and dC at the
+workload's 8192 tokens and hidden size 2048 (1000 classes), and the full
+8192 x 2048 x 128256 workload (sampled rows of dE, a zero-sum property of
+dC; full gradients at 16 rows of the full width).
 """
 import dataclasses
 import math
@@ -156,6 +158,36 @@ def test_full_width_sixteen_rows():
     _check(case, E, C, t, out, what="16 x 2048 x 128256")
 
 
+@pytest.fixture(scope="module")
+def long_tokens():
+    """The linear workload's token count and hidden size (8192 x 2048) with
+    1000 classes (three full 256-class tiles and a ragged one, one
+    vocabulary chunk), and its oracle: small enough for the fp64 oracle to
+    give every element of dE and dC in seconds."""
+    case = _case(8192, 2048, 1000, 2110)
+    E, C, t = S.generate_linear(case, device=DEV)
+    print(f"[linear] oracle for {case.name}", flush=True)
+    ref = linear_oracle_for(E, C, t, ignore_index=case.ignore_index)
+    return case, E, C, t, ref
+
+
+@pytest.mark.parametrize("accum", ["fp32", "kahan"])
+def test_long_token_accumulation_every_element(long_tokens, accum):
+    """dC summed over 8192 tokens at hidden size 2048, the accumulation the
+    apple/ml-cross-entropy issue #14 report finds broken in low precision:
+    every element of dC and dE against the oracle, in both dE modes."""
+    case, E, C, t, ref = long_tokens
+    print(f"[linear] {case.name} accum={accum}", flush=True)
+    out = vce.linear_cross_entropy(E, C, t, ignore_index=case.ignore_index, accum=accum)
+    torch.cuda.synchronize()
+    assert_loss_rows(out["loss_rows"], {"loss_rows": ref["loss_rows"], "status": ref["status"]},
+                     f"long tokens {accum}")
+    assert_scalar_loss(out["loss"].item(), ref["loss"], f"long tokens {accum}")
+    assert int(out["n_valid"].item()) == ref["n_valid"]
+    assert_linear_grad_close(out["dE"], ref["dE"], ref["rsE"], f"long tokens {accum} dE")
+    assert_linear_grad_close(out["dC"], ref["dC"], ref["rsC"], f"long tokens {accum} dC")
+
+
 def test_full_workload_sampled_rows():
     case = S.LINEAR
     E, C, t, out = _run(case)
@@ -176,3 +208,15 @@ def test_full_workload_sampled_rows():
     # every class row of dC is a sum over the valid tokens of G E: with logits
     # of spread about 0.9 every class has gradient mass, so no row is zero
     assert (out["dC"].abs().sum(dim=1) > 0).all()
+    # A property of dC at any size: each row of G sums to zero (softmax minus
+    # a distribution that sums to one), so sum_v dC[v, d] = sum_r E[r, d]
+    # sum_v G[r, v] vanishes up to the bf16 rounding of G, which leaves at
+    # most 2^-9 sum_v |G[r, v]| <= 2^-8 |k_r| per row: the column sums are
+    # bounded by 2^-8 sum_r |k_r| |E[r, d]| (plus fp32 accumulation, far
+    # below).  A dropped or doubled term in any row breaks this.
+    k = 1.0 / n_valid
+    valid = (t != case.ignore_index).to(torch.float64)
+    bound = 2.0 ** -8 * k * (valid[:, None] * E.double().abs()).sum(dim=0)
+    col = out["dC"].double().sum(dim=0)
+    assert torch.all(col.abs() <= bound + 1e-12), \
+        f"dC column sums {col.abs().max().item():.3e} beyond {bound.min().item():.3e}"

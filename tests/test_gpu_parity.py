@@ -432,6 +432,66 @@ def test_minus_inf_logits(dt):
     assert float(out["grad"][2, tgt[2]]) == -1.0
 
 
+@pytest.mark.parametrize("dt,V,eps", [
+    (torch.float32, 700, 0.1),     # fp32 register-resident, fp64 exponentials
+    (torch.bfloat16, 700, 0.1),    # bf16 register-resident with smoothing
+    (torch.float32, 70001, 0.1),   # fp32 rows streamed: online fp64 sums
+    (torch.bfloat16, 700, 0.0),    # bf16 fast path
+])
+def test_plus_inf_logit_gives_nan_row(dt, V, eps):
+    """A +inf non-target logit makes its row's loss NaN (inf - inf in the
+    softmax), as in the oracle; the other rows are unaffected."""
+    c, logits, target = _case(S.PAGE if dt == torch.bfloat16 else S.TINY, 520, V, 909, eps=eps,
+                              dtype=dt)
+    target[0] = 10
+    logits[0, 5] = math.inf
+    target[1] = -100
+    logits[1, 3] = math.inf                   # an ignored row: still exactly zero
+    out = vce.fused_fwd_bwd(logits, target, label_smoothing=eps, reduction="none")
+    torch.cuda.synchronize()
+    ref = P.oracle_for(logits, target, eps=eps, reduction="none")
+    assert math.isnan(ref["loss_rows"][0])
+    lr = out["loss_rows"].cpu()
+    _say(f"[+inf] {dt} V={V} eps={eps}: row 0 loss {lr[0].item()}")
+    assert math.isnan(lr[0].item()), f"+inf row: loss {lr[0].item()} instead of NaN"
+    assert lr[1].item() == 0.0 and torch.all(out["grad"][1] == 0)
+    rest = list(range(2, 520))
+    sub = {k: (v[rest] if isinstance(v, np.ndarray) and v.shape[:1] == (520,) else v)
+           for k, v in ref.items()}
+    P.assert_loss_rows(out["loss_rows"][2:], sub, "+inf other rows")
+    P.assert_grad_close(out["grad"][2:], ref["grad"][2:], "+inf other rows grad")
+
+
+def test_side_stream_calls_match_current_stream():
+    """stream= runs a call on another stream: its outputs and workspace are
+    allocated there, so allocations on the current stream made while it runs
+    cannot take them over.  The split-V grid keeps partial statistics in the
+    workspace; results equal a current-stream call bit for bit and the
+    oracle within the usual bounds."""
+    c, logits, target = _case(S.PAGE, 40, 128256, 905, eps=0.1)
+    ref = vce.fused_fwd_bwd(logits, target, label_smoothing=0.1)
+    f_ref = vce.forward(logits, target, label_smoothing=0.1)
+    g_ref = vce.backward(logits, target, f_ref["fin"], f_ref["n_valid"], label_smoothing=0.1)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    out = vce.fused_fwd_bwd(logits, target, label_smoothing=0.1, stream=s)
+    f = vce.forward(logits, target, label_smoothing=0.1, stream=s)
+    g = vce.backward(logits, target, f["fin"], f["n_valid"], label_smoothing=0.1, stream=s)
+    junk = [torch.full((1 << 22,), 7.0, device=DEV) for _ in range(8)]
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    del junk
+    for k in ("loss", "loss_rows", "n_valid"):
+        assert torch.equal(out[k], ref[k]), k
+    assert torch.equal(out["grad"].view(torch.int16), ref["grad"].view(torch.int16))
+    assert torch.equal(f["loss"], f_ref["loss"])
+    assert torch.equal(g.view(torch.int16), g_ref.view(torch.int16))
+    oracle = P.oracle_for(logits, target, eps=0.1)
+    P.assert_loss_rows(out["loss_rows"], oracle, "side stream")
+    P.assert_grad_close(out["grad"], oracle["grad"], "side stream grad")
+
+
 def test_deterministic_run_to_run():
     c, logits, target = _case(S.PAGE, 700, 50000, 123, eps=0.1)
     a = vce.fused_fwd_bwd(logits, target, label_smoothing=0.1)
@@ -613,14 +673,23 @@ def test_smoothed_gradient_where_p_meets_eps_over_v(eps, V):
 ])
 def test_in_place_gradient_matches_out_of_place(T, V, dt, eps):
     """grad == logits: the gradient overwrites the logits (same pointer,
-    stride and dtype) and equals the out-of-place result bit for bit."""
+    stride and dtype).  Every element of the in-place result is checked
+    against the fp64 oracle on the original logits (kept on the host before
+    the call), and it also equals the out-of-place result bit for bit."""
     c, logits, target = _case(S.PAGE, T, V, 151 + T, eps=eps, dtype=dt)
     _say(f"[in place] T={T} V={V} {dt} eps={eps}")
     ref = vce.fused_fwd_bwd(logits, target, label_smoothing=eps)
+    oracle = P.oracle_for(logits, target, eps=eps)
     buf = logits.clone()
     out = vce.fused_fwd_bwd(buf, target, label_smoothing=eps, grad=buf)
     torch.cuda.synchronize()
     assert out["grad"].data_ptr() == buf.data_ptr()
+    # against the oracle: losses, counts and every gradient element
+    assert int(out["n_valid"].item()) == oracle["n_valid"]
+    P.assert_loss_rows(out["loss_rows"], oracle, f"in place T={T} V={V}")
+    P.assert_scalar_loss(out["loss"].item(), oracle["loss"], f"in place T={T} V={V}")
+    P.assert_grad_close(buf, oracle["grad"], f"in place T={T} V={V} grad")
+    # and the same bits as the out-of-place call
     assert torch.equal(out["loss_rows"], ref["loss_rows"])
     assert torch.equal(out["loss"], ref["loss"])
     assert torch.equal(buf.view(torch.int16 if dt == torch.bfloat16 else torch.int32),
@@ -718,30 +787,37 @@ def test_autograd_cross_entropy(reduction, eps):
     P.assert_grad_close(x.grad, ref["grad"], f"autograd {reduction} grad")
 
 
-def test_fused_events_bracket_the_kernel():
-    """ce_set_fused_events: the events recorded around the fused call's main
-    kernel time it (a positive duration below the whole call's), and the
-    call's results are those of a call without them."""
+def test_timed_call_events_bracket_the_kernel():
+    """ce_fused_fwd_bwd_timed (measurement only): the events it records
+    around the fused call's main kernel time it (a positive duration below
+    the whole call's), and its results are bit-identical to ce_fused_fwd_bwd."""
     c, logits, target = _case(S.PAGE, 600, 128256, 181)
     ref = vce.fused_fwd_bwd(logits, target)
+    T, V = logits.shape
+    prob = vce.make_problem(T, V, ignore_index=c.ignore_index, reduction="mean")
+    nws = vce.ce_workspace_bytes(prob, vce.CE_OP_FUSED)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=DEV)
+    loss = torch.empty(1, dtype=torch.float32, device=DEV)
+    rows = torch.empty(T, dtype=torch.float32, device=DEV)
+    nv = torch.empty(1, dtype=torch.int32, device=DEV)
+    err = torch.empty(1, dtype=torch.int32, device=DEV)
+    grad = torch.empty_like(logits)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     b.record()
     torch.cuda.synchronize()
-    vce.ce_set_fused_events(a.cuda_event, b.cuda_event)
-    try:
-        w0.record()
-        out = vce.fused_fwd_bwd(logits, target)
-        w1.record()
-    finally:
-        vce.ce_set_fused_events(None, None)
+    w0.record()
+    vce.ce_fused_fwd_bwd_timed(prob, logits, vce.CE_BF16, target, None, rows, loss, nv, err,
+                               grad, vce.CE_BF16, V, ws, nws, None, a.cuda_event, b.cuda_event)
+    w1.record()
     torch.cuda.synchronize()
     k, whole = a.elapsed_time(b), w0.elapsed_time(w1)
     _say(f"[events] fused kernel {k * 1e3:.1f} us of a {whole * 1e3:.1f} us call")
     assert 0.0 < k < whole
-    assert torch.equal(out["loss"], ref["loss"])
-    assert torch.equal(out["grad"].view(torch.int16), ref["grad"].view(torch.int16))
+    assert torch.equal(loss, ref["loss"])
+    assert torch.equal(rows, ref["loss_rows"])
+    assert torch.equal(grad.view(torch.int16), ref["grad"].view(torch.int16))
 
 
 @pytest.mark.parametrize("V,eps,out_dt", [(70001, 0.1, torch.float32), (70001, 0.0, torch.bfloat16),

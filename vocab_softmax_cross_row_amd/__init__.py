@@ -6,7 +6,7 @@ from ._binding import (CE_BF16, CE_F32, CE_OP_BACKWARD, CE_OP_FORWARD, CE_OP_FUS
                        CE_OP_MERGE, CE_RED_MEAN, CE_RED_NONE, CE_RED_SUM, CEError,
                        CELinearProblem, CEProblem, ce_backward, ce_forward, ce_fused_fwd_bwd,
                        ce_linear_fwd_bwd, ce_linear_workspace_bytes, ce_merge_shard_stats,
-                       ce_set_fused_events, ce_status_str, ce_version, ce_workspace_bytes,
+                       ce_fused_fwd_bwd_timed, ce_status_str, ce_version, ce_workspace_bytes,
                        make_linear_problem,
                        make_problem, read_final, read_stats)
 from .api import (CrossEntropy, backward, cross_entropy, forward, fused_fwd_bwd,  # noqa: F401

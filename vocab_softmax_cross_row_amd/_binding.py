@@ -28,7 +28,7 @@ REDUCTIONS = {"none": CE_RED_NONE, "sum": CE_RED_SUM, "mean": CE_RED_MEAN}
 # symbols declared in include/vocab_ce.h
 EXPORTS = ("ce_workspace_bytes", "ce_forward", "ce_merge_shard_stats", "ce_backward",
            "ce_fused_fwd_bwd", "ce_linear_workspace_bytes", "ce_linear_fwd_bwd",
-           "ce_status_str", "ce_version", "ce_set_fused_events")
+           "ce_status_str", "ce_version", "ce_fused_fwd_bwd_timed")
 CE_ACC_FP32, CE_ACC_KAHAN = 0, 1
 ACCUMS = {"fp32": CE_ACC_FP32, "kahan": CE_ACC_KAHAN}
 CE_LINEAR_CHUNK = 16384
@@ -94,8 +94,9 @@ def lib():
         L.ce_status_str.restype = ctypes.c_char_p
         L.ce_version.argtypes = []
         L.ce_version.restype = i32
-        L.ce_set_fused_events.argtypes = [P, P]
-        L.ce_set_fused_events.restype = i32
+        L.ce_fused_fwd_bwd_timed.argtypes = [prob, P, i32, P, P, P, P, P, P, P, i32, i64, P, sz, P,
+                                             P, P]
+        L.ce_fused_fwd_bwd_timed.restype = i32
         _lib = L
     return _lib
 
@@ -201,11 +202,17 @@ def ce_version():
     return int(lib().ce_version())
 
 
-def ce_set_fused_events(start, stop):
-    """Events (raw hipEvent_t handles, or None) recorded around the main
-    kernels of later ce_fused_fwd_bwd calls on this host thread."""
-    _check("ce_set_fused_events", lib().ce_set_fused_events(
-        ctypes.c_void_p(start) if start else None, ctypes.c_void_p(stop) if stop else None))
+def ce_fused_fwd_bwd_timed(prob, logits, logits_dtype, target, grad_output, loss_rows, loss,
+                           n_valid, err_count, grad, grad_dtype, ldg, ws, ws_bytes, stream,
+                           ev_start, ev_stop):
+    """Measurement only: ce_fused_fwd_bwd plus two HIP events (raw hipEvent_t
+    handles, or None) recorded around its main kernels."""
+    _check("ce_fused_fwd_bwd_timed", lib().ce_fused_fwd_bwd_timed(
+        ctypes.byref(prob), _ptr(logits), int(logits_dtype), _ptr(target), _ptr(grad_output),
+        _ptr(loss_rows), _ptr(loss), _ptr(n_valid), _ptr(err_count), _ptr(grad),
+        int(grad_dtype), int(ldg), _ptr(ws), int(ws_bytes), _stream(stream),
+        ctypes.c_void_p(ev_start) if ev_start else None,
+        ctypes.c_void_p(ev_stop) if ev_stop else None))
 
 
 def read_stats(raw):

@@ -2,7 +2,16 @@
 the library, return tensors.  No arithmetic happens here; options are
 keyword-only (Megatron-core unfused_cross_entropy passes the process group
 by keyword because the third positional argument is label_smoothing).
+
+``stream``: the torch stream (or raw hipStream_t handle) the call runs on;
+None is torch's current stream.  Outputs and the workspace are allocated
+with that stream current, so torch's caching allocator orders their reuse
+after the call's kernels; inputs made on another stream must be ready on
+this one (the caller's wait, as for any torch op).
 """
+import contextlib
+import functools
+
 import torch
 
 from . import _binding as B
@@ -51,11 +60,31 @@ def _grad_dtype(grad, grad_dtype, logits):
     return grad_dtype or logits.dtype
 
 
+def _on(stream):
+    """Context that makes `stream` current (allocations and the launch go on
+    it), or does nothing for None."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream))
+    return torch.cuda.stream(stream)
+
+
+def _on_stream(fn):
+    """Runs `fn` with its `stream` keyword current (see the module notes)."""
+    @functools.wraps(fn)
+    def run(*args, stream=None, **kw):
+        with _on(stream):
+            return fn(*args, stream=stream, **kw)
+    return run
+
+
 def _workspace(prob, op, device):
     n = B.ce_workspace_bytes(prob, op)
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device), n
 
 
+@_on_stream
 def fused_fwd_bwd(logits, target, *, ignore_index=-100, label_smoothing=0.0, reduction="mean",
                   grad_output=None, grad_dtype=None, grad=None, stream=None):
     """Loss, per-row loss, counts and d loss / d logits in one call."""
@@ -80,6 +109,7 @@ def fused_fwd_bwd(logits, target, *, ignore_index=-100, label_smoothing=0.0, red
             "err_count": err}
 
 
+@_on_stream
 def forward(logits, target, *, vocab_start=0, V_total=None, ignore_index=-100,
             label_smoothing=0.0, reduction="mean", stream=None):
     """Row statistics of this call's columns; when they are the whole
@@ -108,6 +138,7 @@ def forward(logits, target, *, vocab_start=0, V_total=None, ignore_index=-100,
     return out
 
 
+@_on_stream
 def merge_shard_stats(shard_stats, target, V_total, *, ignore_index=-100, label_smoothing=0.0,
                       reduction="mean", stream=None):
     """Merge per-shard statistics (a list of [T, 32] byte buffers in shard
@@ -131,6 +162,7 @@ def merge_shard_stats(shard_stats, target, V_total, *, ignore_index=-100, label_
             "err_count": err}
 
 
+@_on_stream
 def backward(logits, target, fin, n_valid, *, grad_output=None, vocab_start=0, V_total=None,
              ignore_index=-100, label_smoothing=0.0, reduction="mean", grad_dtype=None,
              grad=None, stream=None):
@@ -180,6 +212,7 @@ def cross_entropy(logits, target, *, ignore_index=-100, label_smoothing=0.0, red
     return CrossEntropy.apply(logits, target, ignore_index, label_smoothing, reduction)
 
 
+@_on_stream
 def linear_cross_entropy(E, C, target, *, ignore_index=-100, label_smoothing=0.0,
                          reduction="mean", grad_output=None, backward=True, accum="fp32",
                          stream=None):

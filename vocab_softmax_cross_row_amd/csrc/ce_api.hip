@@ -33,10 +33,6 @@ constexpr int64_t kSmoothedResidentMaxCols = 32768;
 
 constexpr size_t kAlign = 256;
 
-// ce_set_fused_events: events recorded around the fused call's main
-// kernels, per host thread (NULL: off)
-thread_local hipEvent_t g_fused_start = nullptr, g_fused_stop = nullptr;
-
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
@@ -418,10 +414,18 @@ int ce_backward(const ce_problem *prob, const void *logits, int logits_dtype,
     return CE_OK;
 }
 
-int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtype,
-                     const int64_t *target, const float *grad_output, float *loss_rows,
-                     float *loss, int32_t *n_valid, int32_t *err_count, void *grad,
-                     int grad_dtype, int64_t ldg, void *ws, size_t ws_bytes, void *stream) {
+} // extern "C"
+
+namespace {
+
+// ce_fused_fwd_bwd, with optional events recorded on the stream just before
+// and just after the main kernels (everything between the count of valid
+// targets and the loss reduction); NULL events are not recorded.
+int fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtype,
+                  const int64_t *target, const float *grad_output, float *loss_rows, float *loss,
+                  int32_t *n_valid, int32_t *err_count, void *grad, int grad_dtype, int64_t ldg,
+                  void *ws, size_t ws_bytes, hipStream_t s, hipEvent_t ev_start,
+                  hipEvent_t ev_stop) {
     int rc = check_problem(prob);
     if (rc != CE_OK) return rc;
     if (!dtype_ok(logits_dtype) || !dtype_ok(grad_dtype)) return CE_ERR_DTYPE;
@@ -435,13 +439,12 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
         overlaps(logits, matrix_bytes(p.T, p.V_local, p.ld, elem_size(logits_dtype)), grad,
                  matrix_bytes(p.T, p.V_local, ldg, elem_size(grad_dtype))))
         return CE_ERR_ALIAS;
-    hipStream_t s = static_cast<hipStream_t>(stream);
 
     int32_t *nv = n_valid ? n_valid : at<int32_t>(ws, l.n_valid);
     VCE_TRY(launch_count(target, p.T, p.ignore_index, p.V_total, nv, err_count, s));
     float *lr = loss_rows ? loss_rows : at<float>(ws, l.loss_rows);
 
-    if (p.T > 0 && g_fused_start) VCE_TRY(hipEventRecord(g_fused_start, s));
+    if (p.T > 0 && ev_start) VCE_TRY(hipEventRecord(ev_start, s));
     if (p.T > 0) {
         const bool vec = vec_ok(logits, p.ld, logits_dtype, grad, ldg, grad_dtype);
         const bool svec = stream_vec_ok(logits, p.ld, logits_dtype, grad, ldg, grad_dtype);
@@ -528,10 +531,35 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
             VCE_TRY(launch_grad(ga, logits_dtype, grad_dtype, svec, p.T, s));
         }
     }
-    if (p.T > 0 && g_fused_stop) VCE_TRY(hipEventRecord(g_fused_stop, s));
+    if (p.T > 0 && ev_stop) VCE_TRY(hipEventRecord(ev_stop, s));
     if (loss && p.reduction != CE_RED_NONE)
         VCE_TRY(launch_reduce(lr, p.T, p.reduction, nv, loss, s));
     return CE_OK;
+}
+
+} // namespace
+
+extern "C" {
+
+int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtype,
+                     const int64_t *target, const float *grad_output, float *loss_rows,
+                     float *loss, int32_t *n_valid, int32_t *err_count, void *grad,
+                     int grad_dtype, int64_t ldg, void *ws, size_t ws_bytes, void *stream) {
+    return fused_fwd_bwd(prob, logits, logits_dtype, target, grad_output, loss_rows, loss, n_valid,
+                         err_count, grad, grad_dtype, ldg, ws, ws_bytes,
+                         static_cast<hipStream_t>(stream), nullptr, nullptr);
+}
+
+int ce_fused_fwd_bwd_timed(const ce_problem *prob, const void *logits, int logits_dtype,
+                           const int64_t *target, const float *grad_output, float *loss_rows,
+                           float *loss, int32_t *n_valid, int32_t *err_count, void *grad,
+                           int grad_dtype, int64_t ldg, void *ws, size_t ws_bytes, void *stream,
+                           void *ev_start, void *ev_stop) {
+    if ((ev_start == nullptr) != (ev_stop == nullptr)) return CE_ERR_ARG;
+    return fused_fwd_bwd(prob, logits, logits_dtype, target, grad_output, loss_rows, loss, n_valid,
+                         err_count, grad, grad_dtype, ldg, ws, ws_bytes,
+                         static_cast<hipStream_t>(stream), static_cast<hipEvent_t>(ev_start),
+                         static_cast<hipEvent_t>(ev_stop));
 }
 
 size_t ce_linear_workspace_bytes(const ce_linear_problem *prob, int backward) {
@@ -688,12 +716,5 @@ const char *ce_status_str(int status) {
 }
 
 int ce_version(void) { return 100; }
-
-int ce_set_fused_events(void *start, void *stop) {
-    if ((start == nullptr) != (stop == nullptr)) return CE_ERR_ARG;
-    g_fused_start = static_cast<hipEvent_t>(start);
-    g_fused_stop = static_cast<hipEvent_t>(stop);
-    return CE_OK;
-}
 
 } // extern "C"

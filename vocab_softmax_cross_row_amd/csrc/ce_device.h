@@ -41,7 +41,8 @@ __device__ __forceinline__ float ninf() { return -__builtin_inff(); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// e^x in fp64 for x <= 0 (or -inf), to about 4e-14 relative; 0 below -1000.
+// e^x in fp64 for x <= 0 (or -inf), to about 4e-14 relative; 0 below -1000;
+// NaN for NaN (as from inf - inf when a row holds +inf).
 // Additive range reduction x = n ln2 + r (Cody and Waite), with n taken
 // from the low word of x/ln2 + 1.5 2^52, so |r| <= ln2/2; then
 // e^r = 1 + r q(r), q a degree-8 polynomial interpolating (e^r - 1)/r at
@@ -54,7 +55,7 @@ __device__ __forceinline__ double exp_nonpos(double x) {
     constexpr double kShift = 6755399441055744.0; // 1.5 * 2^52
     constexpr double kInvLn2 = 1.4426950408889634;
     constexpr double kLn2 = 0.6931471805599453;
-    x = fmax(x, -1000.0);
+    x = x < -1000.0 ? -1000.0 : x; // keeps NaN (fmax would turn it into -1000)
     const double a = fma(x, kInvLn2, kShift);
     const double n = a - kShift;
     const double r = fma(n, -kLn2, x);
