@@ -289,7 +289,10 @@ def main():
     pairs = []
     for _ in range(args.steps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)  # torch times only events it has seen recorded; the
+        b.record(stream)  # library records them again around the kernel
         pairs.append((a, b))
+    torch.cuda.synchronize()
     for a, b in pairs:
         B.ce_fused_fwd_bwd_timed(prob, logits, B.CE_BF16, target, None, loss_rows, loss, n_valid,
                                  err, grad, B.CE_BF16, V, ws, nws, stream, a.cuda_event,
