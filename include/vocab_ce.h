@@ -215,6 +215,30 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
                      int grad_dtype, int64_t ldg, void *ws, size_t ws_bytes,
                      void *stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and results as ce_fused_fwd_bwd, with no workspace argument.
+ * Its scratch memory is a static device array of CE_NOALLOC_SCRATCH_BYTES
+ * in the library, one per GPU, held until the process ends; the call
+ * allocates nothing.  The caller still passes inputs and outputs.
+ *   - Problems whose ce_workspace_bytes(prob, CE_OP_FUSED) exceeds
+ *     CE_NOALLOC_SCRATCH_BYTES (about 139,000 rows at any row length; fewer
+ *     with label smoothing of bf16 rows, which adds a 51 KB table) return
+ *     CE_ERR_WORKSPACE before any launch.
+ *   - The stream must belong to the current device (CE_ERR_ARG otherwise).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (two streams, two threads) race and give wrong
+ *     results.  Calls in order on one stream are safe; nothing in the
+ *     array needs to start at zero, every byte read is first written by
+ *     the same call.
+ *   - The first call on a device looks the array's address up once
+ *     (hipGetSymbolAddress) and keeps it. */
+#define CE_NOALLOC_SCRATCH_BYTES (8u << 20)
+int ce_fused_fwd_bwd_noalloc(const ce_problem *prob, const void *logits, int logits_dtype,
+                             const int64_t *target, const float *grad_output, float *loss_rows,
+                             float *loss, int32_t *n_valid, int32_t *err_count, void *grad,
+                             int grad_dtype, int64_t ldg, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Cross-entropy of a linear classifier, logits = E C^T never stored.        */
 /* ------------------------------------------------------------------------ */

@@ -98,6 +98,20 @@ def test_header_constants_match_the_binding():
         m = re.search(r"#define\s+" + name + r"\s+(\d+)", hdr)
         assert m, name
         assert int(m.group(1)) == getattr(B, name), name
+    m = re.search(r"#define CE_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.CE_NOALLOC_SCRATCH_BYTES
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch(lib):
+    """Returns CE_ERR_WORKSPACE on the host, before any HIP call, when the
+    fused workspace would not fit the static scratch array."""
+    p = B.make_problem(200000, 1000)
+    assert B.ce_workspace_bytes(p, B.CE_OP_FUSED) > B.CE_NOALLOC_SCRATCH_BYTES
+    assert lib.ce_fused_fwd_bwd_noalloc(ctypes.byref(p), None, 1, None, None, None, None, None,
+                                        None, None, 1, 1000, None) == -6
+    bad = B.make_problem(4, 10, label_smoothing=2.0)
+    assert lib.ce_fused_fwd_bwd_noalloc(ctypes.byref(bad), None, 1, None, None, None, None, None,
+                                        None, None, 1, 10, None) == -3
 
 
 def test_linear_problem_struct_and_workspace(lib):

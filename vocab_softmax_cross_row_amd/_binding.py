@@ -28,7 +28,8 @@ REDUCTIONS = {"none": CE_RED_NONE, "sum": CE_RED_SUM, "mean": CE_RED_MEAN}
 # symbols declared in include/vocab_ce.h
 EXPORTS = ("ce_workspace_bytes", "ce_forward", "ce_merge_shard_stats", "ce_backward",
            "ce_fused_fwd_bwd", "ce_linear_workspace_bytes", "ce_linear_fwd_bwd",
-           "ce_status_str", "ce_version", "ce_fused_fwd_bwd_timed")
+           "ce_status_str", "ce_version", "ce_fused_fwd_bwd_timed", "ce_fused_fwd_bwd_noalloc")
+CE_NOALLOC_SCRATCH_BYTES = 8 << 20
 CE_ACC_FP32, CE_ACC_KAHAN = 0, 1
 ACCUMS = {"fp32": CE_ACC_FP32, "kahan": CE_ACC_KAHAN}
 CE_LINEAR_CHUNK = 16384
@@ -97,6 +98,8 @@ def lib():
         L.ce_fused_fwd_bwd_timed.argtypes = [prob, P, i32, P, P, P, P, P, P, P, i32, i64, P, sz, P,
                                              P, P]
         L.ce_fused_fwd_bwd_timed.restype = i32
+        L.ce_fused_fwd_bwd_noalloc.argtypes = [prob, P, i32, P, P, P, P, P, P, P, i32, i64, P]
+        L.ce_fused_fwd_bwd_noalloc.restype = i32
         _lib = L
     return _lib
 
@@ -200,6 +203,16 @@ def ce_status_str(status):
 
 def ce_version():
     return int(lib().ce_version())
+
+
+def ce_fused_fwd_bwd_noalloc(prob, logits, logits_dtype, target, grad_output, loss_rows, loss,
+                             n_valid, err_count, grad, grad_dtype, ldg, stream=None):
+    """ce_fused_fwd_bwd without a workspace: the library's static per-device
+    scratch array (calls overlapping on one GPU race)."""
+    _check("ce_fused_fwd_bwd_noalloc", lib().ce_fused_fwd_bwd_noalloc(
+        ctypes.byref(prob), _ptr(logits), int(logits_dtype), _ptr(target), _ptr(grad_output),
+        _ptr(loss_rows), _ptr(loss), _ptr(n_valid), _ptr(err_count), _ptr(grad),
+        int(grad_dtype), int(ldg), _stream(stream)))
 
 
 def ce_fused_fwd_bwd_timed(prob, logits, logits_dtype, target, grad_output, loss_rows, loss,

@@ -8,6 +8,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "ce_launch.h"
 #include "vocab_ce.h"
@@ -242,6 +243,35 @@ LinLayout linear_layout(const ce_linear_problem *p, bool backward) {
     }
     l.total = off;
     return l;
+}
+
+// Device memory of ce_fused_fwd_bwd_noalloc: one array per device, loaded
+// with the code object and held until the process ends.  Host code never
+// uses this name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+static __device__ __align__(256) unsigned char scratch[CE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The scratch array's device address on the current device, which must be
+// the stream's device (NULL stream: the current device's default stream).
+int scratch_address(hipStream_t s, void **out) {
+    int dev = 0;
+    if (current_device(&dev) != hipSuccess) return CE_ERR_HIP;
+    if (s) {
+        hipDevice_t sdev = 0;
+        if (hipStreamGetDevice(s, &sdev) != hipSuccess) return CE_ERR_HIP;
+        if ((int)sdev != dev) return CE_ERR_ARG;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return CE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CE_OK;
 }
 
 #define VCE_TRY(expr)                                                                            \
@@ -548,6 +578,21 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
     return fused_fwd_bwd(prob, logits, logits_dtype, target, grad_output, loss_rows, loss, n_valid,
                          err_count, grad, grad_dtype, ldg, ws, ws_bytes,
                          static_cast<hipStream_t>(stream), nullptr, nullptr);
+}
+
+int ce_fused_fwd_bwd_noalloc(const ce_problem *prob, const void *logits, int logits_dtype,
+                             const int64_t *target, const float *grad_output, float *loss_rows,
+                             float *loss, int32_t *n_valid, int32_t *err_count, void *grad,
+                             int grad_dtype, int64_t ldg, void *stream) {
+    int rc = check_problem(prob);
+    if (rc != CE_OK) return rc;
+    if (layout(prob, CE_OP_FUSED).total > (size_t)CE_NOALLOC_SCRATCH_BYTES) return CE_ERR_WORKSPACE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void *ws = nullptr;
+    if ((rc = scratch_address(s, &ws)) != CE_OK) return rc;
+    return fused_fwd_bwd(prob, logits, logits_dtype, target, grad_output, loss_rows, loss, n_valid,
+                         err_count, grad, grad_dtype, ldg, ws, CE_NOALLOC_SCRATCH_BYTES, s,
+                         nullptr, nullptr);
 }
 
 int ce_fused_fwd_bwd_timed(const ce_problem *prob, const void *logits, int logits_dtype,
