@@ -436,13 +436,29 @@ void oracle_linear_forward(const void *E, const void *C, int dtype, int64_t n, i
  *   dC [V, D] = G^T E          (may be NULL)
  *   rsE [n, D] = sqrt(sum_v (G[r,v] C[v,d])^2),
  *   rsC [V, D] = sqrt(sum_r (G[r,v] E[r,d])^2)   (may be NULL): the scales of
- *             the rounding error a bf16 copy of G brings into each sum. */
+ *             the rounding error a bf16 copy of G brings into each sum.
+ *
+ * Gradient filtering (apple/ml-cross-entropy issue #14: the default
+ * implementation filters gradients; impl="cce_exact" turns it off).  The
+ * page does not define the rule; the reading taken: the unscaled gradient
+ * u_rv = d loss_r / d z_rv (softmax minus the smoothed one-hot, the target
+ * entry -sigma(x) + eps (V-1)/V) is cut into blocks of 256 rows x 256
+ * classes, block (i, j) holding rows 256 i .. 256 i + 255 and classes
+ * 256 j .. 256 j + 255 (the last ones ragged); with tau > 0 a block whose
+ * every |u_rv| is below tau is dropped: its G entries are taken as zero in
+ * both contractions.  tau <= 0 keeps every block (the exact gradients).
+ *   keep      [ceil(n/256), ceil(V/256)] int32, 1 kept / 0 dropped (may be NULL)
+ *   block_max same shape, fp64: max |u_rv| over the block (0 for blocks of
+ *             rows whose status is not 1) (may be NULL) */
 void oracle_linear_backward(const void *E, const void *C, int dtype, int64_t n, int64_t D,
                             int64_t V, const int64_t *target, const int32_t *status,
                             const double *x, const double *lse, double eps, const double *k,
-                            double *G, double *dE, double *dC, double *rsE, double *rsC)
+                            double tau, double *G, double *dE, double *dC, double *rsE,
+                            double *rsC, int32_t *keep, double *block_max)
 {
     const double u = eps / (double)V;
+    const int64_t B = 256, nbr = (n + B - 1) / B, nbv = (V + B - 1) / B;
+    /* the unscaled gradient rows */
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < n; ++r) {
         double *g = G + (size_t)r * (size_t)V;
@@ -452,9 +468,38 @@ void oracle_linear_backward(const void *E, const void *C, int dtype, int64_t n, 
         } else {
             linear_row_logits(E, C, dtype, r, D, V, g);
             for (int64_t v = 0; v < V; ++v)
-                g[v] = k[r] * (exp(g[v] - lse[r]) - u);
-            g[target[r]] = k[r] * (-sigmoid(x[r]) + eps * (double)(V - 1) / (double)V);
+                g[v] = exp(g[v] - lse[r]) - u;
+            g[target[r]] = -sigmoid(x[r]) + eps * (double)(V - 1) / (double)V;
         }
+    }
+    /* the block decisions */
+    int32_t *kp = (int32_t *)malloc((size_t)(nbr * nbv) * sizeof(int32_t));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bi = 0; bi < nbr; ++bi) {
+        for (int64_t bj = 0; bj < nbv; ++bj) {
+            double m = 0.0;
+            for (int64_t r = bi * B; r < n && r < (bi + 1) * B; ++r)
+                for (int64_t v = bj * B; v < V && v < (bj + 1) * B; ++v)
+                    m = fmax(m, fabs(G[(size_t)r * (size_t)V + v]));
+            kp[bi * nbv + bj] = (tau <= 0.0) || (m >= tau);
+            if (keep) keep[bi * nbv + bj] = kp[bi * nbv + bj];
+            if (block_max) block_max[bi * nbv + bj] = m;
+        }
+    }
+    /* scaled by k_r; dropped blocks are zero */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r) {
+        double *g = G + (size_t)r * (size_t)V;
+        if (status[r] != 1)
+            continue;
+        for (int64_t v = 0; v < V; ++v)
+            g[v] = kp[(r / B) * nbv + v / B] ? k[r] * g[v] : 0.0;
+    }
+    free(kp);
+    /* dE[r, d] = sum over v of G[r, v] C[v, d] */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; ++r) {
+        const double *g = G + (size_t)r * (size_t)V;
         for (int64_t d = 0; d < D && (dE || rsE); ++d) {
             double acc = 0.0, sq = 0.0;
             for (int64_t v = 0; v < V; ++v) {

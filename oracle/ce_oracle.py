@@ -56,8 +56,8 @@ def _load():
         lib.oracle_to_bf16.restype = None
         lib.oracle_linear_forward.argtypes = [P, P, i, i64, i64, i64, P, i64, d, P, P, P, P]
         lib.oracle_linear_forward.restype = None
-        lib.oracle_linear_backward.argtypes = [P, P, i, i64, i64, i64, P, P, P, P, d, P,
-                                               P, P, P, P, P]
+        lib.oracle_linear_backward.argtypes = [P, P, i, i64, i64, i64, P, P, P, P, d, P, d,
+                                               P, P, P, P, P, P, P]
         lib.oracle_linear_backward.restype = None
         lib.oracle_threads.argtypes = []
         lib.oracle_threads.restype = i
@@ -202,14 +202,18 @@ def _matrix_args(a):
 
 
 def linear_fwd_bwd(E, C, target, *, ignore_index=-100, eps=0.0, reduction="mean",
-                   grad_output=1.0, n_valid=None, grads=True, dC=True, scales=True):
+                   grad_output=1.0, n_valid=None, grads=True, dC=True, scales=True,
+                   filter_eps=0.0):
     """Cross-entropy of the logits E C^T (apple/ml-cross-entropy issue #14,
     linear_cross_entropy): E [n, D] and C [V, D] of one dtype (bf16 bits as
     uint16, float32 or float64).  Returns loss, loss_rows, status, n_valid,
     lse, and with ``grads`` the fp64 G [n, V], dE [n, D], dC [V, D] (unless
     ``dC`` is False) and the root-sum-square scales rsE, rsC (with
     ``scales``).  ``n_valid`` overrides the mean's denominator when E holds a
-    sample of the rows of a larger batch."""
+    sample of the rows of a larger batch.  ``filter_eps`` > 0 applies
+    gradient filtering (256 x 256 blocks of the unscaled gradient whose
+    entries are all below it in magnitude are dropped, see ce_oracle.c);
+    then ``keep`` and ``block_max`` give the block decisions."""
     E, code = _matrix_args(E)
     C, code_c = _matrix_args(C)
     if code != code_c or E.shape[1] != C.shape[1]:
@@ -236,10 +240,14 @@ def linear_fwd_bwd(E, C, target, *, ignore_index=-100, eps=0.0, reduction="mean"
     dCo = np.empty((V, D), np.float64) if dC else None
     rsE = np.empty((n, D), np.float64) if scales else None
     rsC = np.empty((V, D), np.float64) if (scales and dC) else None
+    nb = ((n + 255) // 256, (V + 255) // 256)
+    keep = np.empty(nb, np.int32)
+    bmax = np.empty(nb, np.float64)
     lib.oracle_linear_backward(_ptr(E), _ptr(C), code, n, D, V, _ptr(target), _ptr(status),
                                _ptr(x), _ptr(lse), float(eps), _ptr(np.ascontiguousarray(k)),
-                               _ptr(G), _ptr(dE), _ptr(dCo), _ptr(rsE), _ptr(rsC))
-    out.update(G=G, dE=dE, dC=dCo, rsE=rsE, rsC=rsC, k=k)
+                               float(filter_eps), _ptr(G), _ptr(dE), _ptr(dCo), _ptr(rsE),
+                               _ptr(rsC), _ptr(keep), _ptr(bmax))
+    out.update(G=G, dE=dE, dC=dCo, rsE=rsE, rsC=rsC, k=k, keep=keep, block_max=bmax)
     return out
 
 

@@ -140,3 +140,72 @@ def test_ignored_and_bad_rows():
     keep = [r for r in range(6) if r not in (1, 3)]
     o2 = O.linear_fwd_bwd(E[keep], C, t[keep], reduction="sum")
     assert np.allclose(o["dC"], o2["dC"], rtol=1e-13, atol=1e-16)
+
+
+def _filter_case(seed):
+    """300 rows x 600 classes (2 x 3 blocks of 256, both ragged), D = 8, in
+    fp64.  Rows 0..255 draw targets from classes 0..255 and rows 256..299
+    from 512..599, so blocks (0, 0) and (1, 2) hold targets (|u| near 1) and
+    the other four hold only softmax values of at most about 3.5e-3, more
+    than 2 times below 2^-7: every decision has a wide margin."""
+    rng = np.random.default_rng(seed)
+    n, V, D = 300, 600, 8
+    E = rng.standard_normal((n, D))
+    C = rng.standard_normal((V, D)) * 0.05
+    t = np.concatenate([rng.integers(0, 256, 256), rng.integers(512, 600, n - 256)])
+    t[7] = -100
+    return E, C, t
+
+
+@pytest.mark.parametrize("eps,reduction,go", [(0.0, "mean", 1.0), (0.1, "sum", 0.5)])
+def test_gradient_filtering_against_independent_blocks(eps, reduction, go):
+    """Gradient filtering (the reading: drop 256 x 256 blocks of the unscaled
+    gradient whose entries are all below tau) against the same rule applied
+    by hand to torch's float64 autograd gradient of cross_entropy(E C^T):
+    block maxima, keep mask, and dE, dC from the masked gradient by numpy."""
+    tau = 2.0 ** -7
+    E, C, t = _filter_case(5)
+    o = O.linear_fwd_bwd(E, C, t, eps=eps, reduction=reduction, grad_output=go, filter_eps=tau)
+    z = torch.tensor(E @ C.T, requires_grad=True)
+    loss = torch.nn.functional.cross_entropy(z, torch.tensor(t), ignore_index=-100,
+                                             label_smoothing=eps, reduction=reduction)
+    loss.backward(torch.tensor(go, dtype=torch.float64))
+    G = z.grad.numpy()
+    k = go if reduction == "sum" else go / int((t != -100).sum())
+    U = np.abs(G / k)
+    n, V = G.shape
+    bm = np.zeros((2, 3))
+    for i in range(2):
+        for j in range(3):
+            bm[i, j] = U[256 * i:256 * (i + 1), 256 * j:256 * (j + 1)].max()
+    assert np.allclose(o["block_max"], bm, rtol=1e-12, atol=1e-15)
+    keep = bm >= tau
+    assert keep.any() and (~keep).any()
+    assert np.all((bm < tau / 2) | (bm > 2 * tau)), "a decision too close to the threshold"
+    assert np.array_equal(o["keep"], keep.astype(np.int32))
+    Gf = G.copy()
+    for i in range(2):
+        for j in range(3):
+            if not keep[i, j]:
+                Gf[256 * i:256 * (i + 1), 256 * j:256 * (j + 1)] = 0.0
+    assert np.allclose(o["G"], Gf, rtol=1e-11, atol=1e-17)
+    assert np.allclose(o["dE"], Gf @ C, rtol=1e-10, atol=1e-15)
+    assert np.allclose(o["dC"], Gf.T @ E, rtol=1e-10, atol=1e-15)
+    # and the filtered result really differs from the exact one
+    ex = O.linear_fwd_bwd(E, C, t, eps=eps, reduction=reduction, grad_output=go)
+    assert np.abs(ex["dC"] - o["dC"]).max() > 1e-6 * np.abs(ex["dC"]).max()
+
+
+def test_gradient_filtering_limits():
+    """tau = 0 is the exact path bit for bit; a tau above every entry drops
+    every block (zero gradients), the loss untouched either way."""
+    E, C, t = _filter_case(6)
+    ex = O.linear_fwd_bwd(E, C, t)
+    z0 = O.linear_fwd_bwd(E, C, t, filter_eps=0.0)
+    for key in ("G", "dE", "dC", "loss_rows"):
+        assert np.array_equal(ex[key], z0[key]), key
+    assert np.all(z0["keep"] == 1)
+    big = O.linear_fwd_bwd(E, C, t, filter_eps=2.0)
+    assert np.all(big["keep"] == 0)
+    assert np.all(big["dE"] == 0.0) and np.all(big["dC"] == 0.0)
+    assert np.array_equal(big["loss_rows"], ex["loss_rows"])
