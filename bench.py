@@ -43,7 +43,8 @@ Objects in the line besides the contract's keys:
   linear_ce     cross-entropy of a linear classifier without stored logits
                 (ce_linear_fwd_bwd): E [8192, 2048] and C [128256, 2048] bf16,
                 loss + dE + dC; MFMA roofline: 4 products of 2 N V D flops
-                against the 2.5 PFLOP/s dense bf16 peak.
+                against the 2.5 PFLOP/s dense bf16 peak; "filtered": the same
+                call with gradient filtering at 2^-8 and the time it saves.
   memory        peak device memory (torch allocator) of one call of each
                 path, inputs included.
 """
@@ -478,7 +479,28 @@ def main():
             inputs["linear"] = {"E_sha256": sha256_of(E), "C_sha256": sha256_of(Cw),
                                 "target_sha256": sha256_of(tl), "seed": lc.seed}
         say(f"# linear CE: {lms:.3f} ms/step, {tfs:.1f} TFLOP/s, workspace {nlw / GIB:.3f} GiB")
-        del lws, dE, dC
+
+        # the same call with gradient filtering at 2^-8 (256 x 256 blocks of
+        # softmax - q whose entries are all below it skipped in the backward)
+        tau = 2.0 ** -8
+        fp = B.make_linear_problem(lc.N, lc.D, lc.V, ignore_index=lc.ignore_index,
+                                   filter_eps=tau)
+        nfw_ = B.ce_linear_workspace_bytes(fp, 1)
+        fws = torch.empty(nfw_, dtype=torch.uint8, device=dev)
+
+        def filtered_step():
+            B.ce_linear_fwd_bwd(fp, E, Cw, tl, None, lrows, loss, n_valid, err, dE, dC, fws,
+                                nfw_, stream)
+
+        fper, fspan, _ = time_steps(filtered_step, klin, 2, stream)
+        fms = fspan / klin
+        linear["filtered"] = {
+            "filter_eps": tau, "ms_per_step": round(fms, 3), "timing": stats_ms(fper),
+            "saved_ms": round(lms - fms, 3), "speedup": round(lms / fms, 3),
+            "TFLOP/s_of_exact_flops": round(flops / (fms * 1e-3) / 1e12, 1),
+            "workspace_bytes": nfw_}
+        say(f"# linear CE filtered at 2^-8: {fms:.3f} ms/step ({lms / fms:.3f}x)")
+        del lws, fws, dE, dC
 
     memory = None
     if not args.no_memory:

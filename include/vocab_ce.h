@@ -247,8 +247,8 @@ int ce_fused_fwd_bwd_noalloc(const ce_problem *prob, const void *logits, int log
  * classifier weight, labels) fuses the classifier product with the loss so
  * that the [N, V] logits are never materialised; the thread's fix keeps the
  * dC and dE accumulations out of low precision (fp32 accumulators, optional
- * Kahan compensation: use_kahan, impl="cce_exact", which also turns off
- * gradient filtering -- no filtering is done here).
+ * Kahan compensation: use_kahan; impl="cce_exact" also turns off gradient
+ * filtering, which is opt-in here through filter_eps).
  *
  *   z_rv = sum_d E[r,d] C[v,d]     (bf16 inputs, fp32 accumulation, MFMA)
  *   loss_r, the 1/4 target select, ignore_index, label smoothing and the
@@ -276,8 +276,22 @@ typedef struct {
     float label_smoothing;/* eps in [0, 1) */
     int32_t reduction;    /* ce_reduction */
     int32_t accum;        /* ce_accum */
-    int32_t reserved;     /* 0 */
+    float filter_eps;     /* gradient filtering threshold; 0 = off (exact) */
 } ce_linear_problem;
+
+/* Gradient filtering (filter_eps > 0; apple/ml-cross-entropy issue #14:
+ * the fused loss filters gradients by default, and impl="cce_exact" turns
+ * that off -- the page does not state the rule; this is the reading taken):
+ * the unscaled gradient u = softmax(z) - q (G = k u, target entries from
+ * the 1/4 select) is cut into blocks of 256 tokens x 256 classes aligned at
+ * token 0 and class 0; a block in which every entry of every valid row has
+ * |u| < filter_eps is dropped -- taken as zero in both backward products,
+ * whose work for it is skipped.  The loss is exact either way.  2^-8 (the
+ * bf16 unit roundoff) drops blocks whose entries all vanish next to a unit
+ * entry at bf16 resolution.  The error this brings into an entry of dE or
+ * dC is at most the sum over the dropped blocks' entries of |G| times the
+ * matching |C| or |E| entries.  filter_eps = 0 gives results bit-identical
+ * to a call without filtering.  Must be finite and >= 0 (else CE_ERR_ARG). */
 
 /* Workspace bytes ce_linear_fwd_bwd needs; `backward` = 0 when dE and dC
  * are both NULL (loss only).  Host function; 0 for an invalid problem. */
@@ -295,7 +309,8 @@ size_t ce_linear_workspace_bytes(const ce_linear_problem *prob, int backward);
  * Errors: CE_ERR_NULL (E, C or target NULL, or only one of dE and dC),
  * CE_ERR_SHAPE (N < 0, D < 8 or not a multiple of 8, V < 1, sizes beyond
  * the kernels' 32-bit block offsets), CE_ERR_SMOOTHING, CE_ERR_REDUCTION,
- * CE_ERR_ARG (unknown accum), CE_ERR_WORKSPACE, CE_ERR_HIP. */
+ * CE_ERR_ARG (unknown accum, filter_eps negative or not finite),
+ * CE_ERR_WORKSPACE, CE_ERR_HIP. */
 int ce_linear_fwd_bwd(const ce_linear_problem *prob, const void *E, const void *C,
                       const int64_t *target, const float *grad_output, float *loss_rows,
                       float *loss, int32_t *n_valid, int32_t *err_count, float *dE, float *dC,

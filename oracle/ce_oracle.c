@@ -380,14 +380,27 @@ double oracle_reduce(const double *loss, const int32_t *status, int64_t n, int r
  * contractions as plain sums.  E and C share one dtype (bf16, fp32 or fp64;
  * fp64 inputs serve the finite-difference checks). */
 
-/* z[v] = E_r . C_v for v in [0, V) */
-static void linear_row_logits(const void *E, const void *C, int dtype, int64_t r, int64_t D,
-                              int64_t V, double *z)
+/* A matrix [rows, cols] as exact doubles, row-major (the caller frees). */
+static double *decode_matrix(const void *X, int dtype, int64_t rows, int64_t cols)
 {
+    const int64_t n = rows * cols;
+    double *out = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = load_elem(X, dtype, i);
+    return out;
+}
+
+/* z[v] = E_r . C_v for v in [0, V), the sum over d in increasing order */
+static void linear_row_logits(const double *E, const double *C, int64_t r, int64_t D, int64_t V,
+                              double *z)
+{
+    const double *e = E + (size_t)r * (size_t)D;
     for (int64_t v = 0; v < V; ++v) {
+        const double *c = C + (size_t)v * (size_t)D;
         double acc = 0.0;
         for (int64_t d = 0; d < D; ++d)
-            acc += load_elem(E, dtype, r * D + d) * load_elem(C, dtype, v * D + d);
+            acc += e[d] * c[d];
         z[v] = acc;
     }
 }
@@ -398,6 +411,7 @@ void oracle_linear_forward(const void *E, const void *C, int dtype, int64_t n, i
                            int64_t V, const int64_t *target, int64_t ignore_index, double eps,
                            double *loss, int32_t *status, double *x_out, double *lse_out)
 {
+    double *Ed = decode_matrix(E, dtype, n, D), *Cd = decode_matrix(C, dtype, V, D);
 #pragma omp parallel
     {
         double *z = (double *)malloc((size_t)V * sizeof(double));
@@ -414,7 +428,7 @@ void oracle_linear_forward(const void *E, const void *C, int dtype, int64_t n, i
             } else {
                 double m, s, zt, sz;
                 int32_t own;
-                linear_row_logits(E, C, dtype, r, D, V, z);
+                linear_row_logits(Ed, Cd, r, D, V, z);
                 shard_row_stats(z, ORACLE_F64, V, t, &m, &s, &zt, &own, &sz);
                 finalize_row(m, s, zt, sz, V, eps, &f);
                 st = 1;
@@ -426,6 +440,8 @@ void oracle_linear_forward(const void *E, const void *C, int dtype, int64_t n, i
         }
         free(z);
     }
+    free(Ed);
+    free(Cd);
 }
 
 /* Gradients, from the status, x and lse oracle_linear_forward returned and
@@ -458,6 +474,7 @@ void oracle_linear_backward(const void *E, const void *C, int dtype, int64_t n, 
 {
     const double u = eps / (double)V;
     const int64_t B = 256, nbr = (n + B - 1) / B, nbv = (V + B - 1) / B;
+    double *Ed = decode_matrix(E, dtype, n, D), *Cd = decode_matrix(C, dtype, V, D);
     /* the unscaled gradient rows */
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < n; ++r) {
@@ -466,7 +483,7 @@ void oracle_linear_backward(const void *E, const void *C, int dtype, int64_t n, 
             for (int64_t v = 0; v < V; ++v)
                 g[v] = 0.0;
         } else {
-            linear_row_logits(E, C, dtype, r, D, V, g);
+            linear_row_logits(Ed, Cd, r, D, V, g);
             for (int64_t v = 0; v < V; ++v)
                 g[v] = exp(g[v] - lse[r]) - u;
             g[target[r]] = -sigmoid(x[r]) + eps * (double)(V - 1) / (double)V;
@@ -496,23 +513,41 @@ void oracle_linear_backward(const void *E, const void *C, int dtype, int64_t n, 
             g[v] = kp[(r / B) * nbv + v / B] ? k[r] * g[v] : 0.0;
     }
     free(kp);
-    /* dE[r, d] = sum over v of G[r, v] C[v, d] */
-#pragma omp parallel for schedule(dynamic, 1)
-    for (int64_t r = 0; r < n; ++r) {
-        const double *g = G + (size_t)r * (size_t)V;
-        for (int64_t d = 0; d < D && (dE || rsE); ++d) {
-            double acc = 0.0, sq = 0.0;
-            for (int64_t v = 0; v < V; ++v) {
-                const double p = g[v] * load_elem(C, dtype, v * D + d);
-                acc += p;
-                sq += p * p;
+    /* dE[r, d] = sum over v = 0, 1, ..., V-1 of G[r, v] C[v, d]: the D sums
+     * of a row advance together, v in the outer loop, so C is read row by
+     * row; each sum still takes its terms in increasing v. */
+    if (dE || rsE) {
+#pragma omp parallel
+        {
+            double *acc = (double *)malloc((size_t)D * sizeof(double));
+            double *sq = (double *)malloc((size_t)D * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < n; ++r) {
+                const double *g = G + (size_t)r * (size_t)V;
+                for (int64_t d = 0; d < D; ++d)
+                    acc[d] = sq[d] = 0.0;
+                for (int64_t v = 0; v < V; ++v) {
+                    const double *c = Cd + (size_t)v * (size_t)D;
+                    for (int64_t d = 0; d < D; ++d) {
+                        const double p = g[v] * c[d];
+                        acc[d] += p;
+                        sq[d] += p * p;
+                    }
+                }
+                for (int64_t d = 0; d < D; ++d) {
+                    if (dE) dE[r * D + d] = acc[d];
+                    if (rsE) rsE[r * D + d] = sqrt(sq[d]);
+                }
             }
-            if (dE) dE[r * D + d] = acc;
-            if (rsE) rsE[r * D + d] = sqrt(sq);
+            free(acc);
+            free(sq);
         }
     }
-    if (!dC && !rsC)
+    free(Cd);
+    if (!dC && !rsC) {
+        free(Ed);
         return;
+    }
     /* dC[v, d] = sum over r = 0, 1, ..., n-1 of G[r, v] E[r, d].  Column v of G
      * and column d of E are first copied out contiguously, so the sum walks
      * memory in order; the terms and their order are those of the definition. */
@@ -525,7 +560,8 @@ void oracle_linear_backward(const void *E, const void *C, int dtype, int64_t n, 
 #pragma omp parallel for schedule(static)
     for (int64_t d = 0; d < D; ++d)
         for (int64_t r = 0; r < n; ++r)
-            ET[(size_t)d * (size_t)n + r] = load_elem(E, dtype, r * D + d);
+            ET[(size_t)d * (size_t)n + r] = Ed[(size_t)r * (size_t)D + d];
+    free(Ed);
 #pragma omp parallel for schedule(dynamic, 4)
     for (int64_t v = 0; v < V; ++v) {
         const double *gv = GT + (size_t)v * (size_t)n;

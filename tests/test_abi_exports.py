@@ -127,11 +127,18 @@ def test_linear_problem_struct_and_workspace(lib):
     assert B.ce_linear_workspace_bytes(k, 1) >= both + 8192 * 2048 * 4
     assert B.ce_linear_workspace_bytes(B.make_linear_problem(4, 12, 10), 0) == 0  # D % 8
     assert B.ce_linear_workspace_bytes(B.make_linear_problem(4, 16, 10, accum=5), 0) == 0
+    # gradient filtering adds its per-chunk flags and lists to the backward only
+    f = B.make_linear_problem(8192, 2048, 128256, filter_eps=2.0 ** -8)
+    tiles = (8192 // 256) * (B.CE_LINEAR_CHUNK // 256)
+    assert B.ce_linear_workspace_bytes(f, 1) >= both + tiles * (16 + 4)
+    assert B.ce_linear_workspace_bytes(f, 0) == fwd
 
 
 @pytest.mark.parametrize("kw,status", [
     (dict(D=12), -2), (dict(D=0), -2), (dict(V=0), -2), (dict(N=-1), -2),
     (dict(label_smoothing=1.0), -3), (dict(reduction=9), -5), (dict(accum=3), -10),
+    (dict(filter_eps=-1.0), -10), (dict(filter_eps=float("nan")), -10),
+    (dict(filter_eps=float("inf")), -10),
 ])
 def test_linear_argument_checks_before_any_launch(lib, kw, status):
     args = dict(N=4, D=16, V=10)

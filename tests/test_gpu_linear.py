@@ -220,3 +220,106 @@ def test_full_workload_sampled_rows():
     col = out["dC"].double().sum(dim=0)
     assert torch.all(col.abs() <= bound + 1e-12), \
         f"dC column sums {col.abs().max().item():.3e} beyond {bound.min().item():.3e}"
+
+
+# --------------------------------------------------------------------------
+# gradient filtering (filter_eps > 0)
+# --------------------------------------------------------------------------
+TAU = 2.0 ** -8
+
+
+def _targets_in(t, ranges, seed):
+    """Redraw the non-ignored targets uniformly from the union of `ranges`,
+    leaving class tiles outside them without targets (their blocks then
+    hold only softmax values far below TAU)."""
+    g = torch.Generator().manual_seed(seed)
+    pool = torch.cat([torch.arange(a, b) for a, b in ranges])
+    t = t.clone().cpu()
+    keep = t != -100
+    t[keep] = pool[torch.randint(0, len(pool), (int(keep.sum()),), generator=g)]
+    return t.to(DEV)
+
+
+@pytest.mark.parametrize("accum", ["fp32", "kahan"])
+def test_filtering_that_keeps_every_block_is_exact(accum):
+    """A threshold below every entry keeps every block: the filtered K walk
+    (lists of kept tiles) must then reproduce the unfiltered products bit
+    for bit: 3 token tiles (the last ragged), 2 vocabulary chunks."""
+    case = _case(600, 256, B.CE_LINEAR_CHUNK + 700, 2120)
+    E, C, t = S.generate_linear(case, device=DEV)
+    a = vce.linear_cross_entropy(E, C, t, accum=accum)
+    b = vce.linear_cross_entropy(E, C, t, accum=accum, filter_eps=1e-30)
+    torch.cuda.synchronize()
+    for k in ("loss", "loss_rows", "dE", "dC"):
+        assert torch.equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("eps,reduction,accum,go", [(0.0, "mean", "fp32", None),
+                                                    (0.1, "sum", "kahan", 0.5)])
+def test_filtering_against_oracle(eps, reduction, accum, go):
+    """Filtering at 2^-8 on 556 tokens x 18384 classes (two chunks, ragged
+    in tokens and classes), targets drawn from classes 0..1499 and
+    16400..17099 only: the blocks of the other class tiles hold softmax
+    values near 1/V and are dropped, the others are kept.  The oracle applies
+    the same rule; every decision is first checked to sit far from the
+    threshold, then dE and dC are compared with the filtered oracle at the
+    usual bound, and they must differ from the unfiltered result."""
+    case = _case(556, 256, B.CE_LINEAR_CHUNK + 2000, 2121, eps=eps, reduction=reduction)
+    E, C, t = S.generate_linear(case, device=DEV)
+    t = _targets_in(t, [(0, 1500), (16400, 17100)], 2122)
+    gout = None if go is None else torch.tensor([go], device=DEV)
+    print(f"[linear filter] eps={eps} {reduction} {accum}", flush=True)
+    out = vce.linear_cross_entropy(E, C, t, label_smoothing=eps, reduction=reduction,
+                                   grad_output=gout, accum=accum, filter_eps=TAU)
+    exact = vce.linear_cross_entropy(E, C, t, label_smoothing=eps, reduction=reduction,
+                                     grad_output=gout, accum=accum)
+    torch.cuda.synchronize()
+    ref = linear_oracle_for(E, C, t, eps=eps, reduction=reduction,
+                            grad_output=1.0 if go is None else go)
+    Eb = E.cpu().view(torch.int16).numpy().view(np.uint16)
+    Cb = C.cpu().view(torch.int16).numpy().view(np.uint16)
+    from oracle import ce_oracle as O
+    fref = O.linear_fwd_bwd(Eb, Cb, t.cpu().numpy(), eps=float(np.float32(eps)),
+                            reduction=reduction, grad_output=1.0 if go is None else go,
+                            filter_eps=TAU)
+    bm = fref["block_max"]
+    assert np.all((bm < TAU / 2) | (bm > 2 * TAU)), "a block decision too close to the threshold"
+    assert fref["keep"].any() and not fref["keep"].all()
+    assert_loss_rows(out["loss_rows"], {"loss_rows": ref["loss_rows"], "status": ref["status"]},
+                     "filtered")
+    assert torch.equal(out["loss_rows"], exact["loss_rows"])
+    assert_linear_grad_close(out["dE"], fref["dE"], fref["rsE"], "filtered dE")
+    assert_linear_grad_close(out["dC"], fref["dC"], fref["rsC"], "filtered dC")
+    assert not torch.equal(out["dC"], exact["dC"])
+    # rows of dC whose class tiles were dropped for every token tile are zero
+    dropped_cols = np.nonzero(fref["keep"].max(axis=0) == 0)[0]
+    assert len(dropped_cols) > 0
+    for j in dropped_cols[:3]:
+        assert torch.all(out["dC"][256 * j:256 * (j + 1)] == 0)
+
+
+def test_filtering_full_workload_one_token_tile():
+    """The full 8192 x 2048 x 128256 workload with filtering at 2^-8, in the
+    launch configuration of the benchmark: every dE entry of one token tile
+    (rows 2048 .. 2303; a block's decision depends only on its own 256
+    rows) against the oracle applying the same rule to those rows, with the
+    batch's N_valid for the mean."""
+    case = S.LINEAR
+    E, C, t = S.generate_linear(case, device=DEV)
+    out = vce.linear_cross_entropy(E, C, t, filter_eps=TAU)
+    torch.cuda.synchronize()
+    n_valid = int((t != case.ignore_index).sum().item())
+    rows = slice(2048, 2304)
+    Eb = E[rows].cpu().view(torch.int16).numpy().view(np.uint16)
+    Cb = C.cpu().view(torch.int16).numpy().view(np.uint16)
+    from oracle import ce_oracle as O
+    print("[linear filter] oracle for one token tile at full width", flush=True)
+    fref = O.linear_fwd_bwd(Eb, Cb, t[rows].cpu().numpy(), n_valid=n_valid, dC=False,
+                            filter_eps=TAU)
+    bm = fref["block_max"]
+    assert np.all((bm < TAU / 2) | (bm > 2 * TAU)), "a block decision too close to the threshold"
+    print(f"[linear filter] {int(fref['keep'].sum())} of {fref['keep'].size} blocks kept",
+          flush=True)
+    assert_loss_rows(out["loss_rows"][rows], {"loss_rows": fref["loss_rows"],
+                                              "status": fref["status"]}, "filtered full")
+    assert_linear_grad_close(out["dE"][rows], fref["dE"], fref["rsE"], "filtered full dE")

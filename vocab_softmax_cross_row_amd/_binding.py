@@ -53,7 +53,7 @@ class CELinearProblem(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int64), ("D", ctypes.c_int64), ("V", ctypes.c_int64),
                 ("ignore_index", ctypes.c_int64), ("label_smoothing", ctypes.c_float),
                 ("reduction", ctypes.c_int32), ("accum", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("filter_eps", ctypes.c_float)]
 
 
 class CEError(RuntimeError):
@@ -178,11 +178,11 @@ def ce_fused_fwd_bwd(prob, logits, logits_dtype, target, grad_output, loss_rows,
 
 
 def make_linear_problem(N, D, V, *, ignore_index=-100, label_smoothing=0.0, reduction="mean",
-                        accum="fp32"):
+                        accum="fp32", filter_eps=0.0):
     red = REDUCTIONS[reduction] if isinstance(reduction, str) else int(reduction)
     acc = ACCUMS[accum] if isinstance(accum, str) else int(accum)
     return CELinearProblem(int(N), int(D), int(V), int(ignore_index), float(label_smoothing),
-                           red, acc, 0)
+                           red, acc, float(filter_eps))
 
 
 def ce_linear_workspace_bytes(prob, backward):

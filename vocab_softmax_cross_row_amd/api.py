@@ -215,11 +215,13 @@ def cross_entropy(logits, target, *, ignore_index=-100, label_smoothing=0.0, red
 @_on_stream
 def linear_cross_entropy(E, C, target, *, ignore_index=-100, label_smoothing=0.0,
                          reduction="mean", grad_output=None, backward=True, accum="fp32",
-                         stream=None):
+                         filter_eps=0.0, stream=None):
     """Cross-entropy of the logits E C^T without forming them (the library's
     ce_linear_fwd_bwd): E [N, D] and C [V, D] bf16 with contiguous rows.
     Returns loss, loss_rows, n_valid, err_count and, with ``backward``, the
-    fp32 gradients dE [N, D] and dC [V, D]."""
+    fp32 gradients dE [N, D] and dC [V, D].  ``filter_eps`` > 0 turns on
+    gradient filtering (256 x 256 blocks of softmax - q below it dropped
+    from the backward products; 0, the default, is exact)."""
     if E.dtype != torch.bfloat16 or C.dtype != torch.bfloat16:
         raise ValueError("E and C must be bf16")
     if E.dim() != 2 or C.dim() != 2 or E.shape[1] != C.shape[1]:
@@ -232,7 +234,7 @@ def linear_cross_entropy(E, C, target, *, ignore_index=-100, label_smoothing=0.0
     dev = E.device
     prob = B.make_linear_problem(N, D, V, ignore_index=ignore_index,
                                  label_smoothing=label_smoothing, reduction=reduction,
-                                 accum=accum)
+                                 accum=accum, filter_eps=filter_eps)
     nws = B.ce_linear_workspace_bytes(prob, backward)
     ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=dev)
     loss = torch.empty(1, dtype=torch.float32, device=dev)

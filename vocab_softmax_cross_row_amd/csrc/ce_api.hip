@@ -191,6 +191,7 @@ int check_linear(const ce_linear_problem *p) {
         p->label_smoothing >= 1.0f)
         return CE_ERR_SMOOTHING;
     if (p->accum != CE_ACC_FP32 && p->accum != CE_ACC_KAHAN) return CE_ERR_ARG;
+    if (!std::isfinite(p->filter_eps) || p->filter_eps < 0.0f) return CE_ERR_ARG;
     if (p->N < 0 || p->D < 8 || p->D % 8 != 0 || p->V < 1) return CE_ERR_SHAPE;
     // fragment-major operands: 8 row blocks of 32 rows x (padded K) bf16 must
     // stay below 2^31 bytes (32-bit buffer offsets); counts are int32
@@ -209,7 +210,9 @@ struct LinLayout {
     int64_t Vp;  // classes padded to 256: rows of Cf, K of CTf
     int64_t Vc;  // classes per backward chunk
     int64_t tiles_v;
-    size_t Ef, Cf, stats, fin, loss_rows, counts, ETf, CTf, rows, G, GT, comp, total;
+    size_t Ef, Cf, stats, fin, loss_rows, counts, ETf, CTf, rows, G, GT, comp;
+    size_t flags, list_e, cnt_e, list_c, cnt_c; // gradient filtering, per chunk
+    size_t total;
 };
 
 LinLayout linear_layout(const ce_linear_problem *p, bool backward) {
@@ -240,6 +243,14 @@ LinLayout linear_layout(const ce_linear_problem *p, bool backward) {
         l.G = take((size_t)l.Np * l.Vc * 2);
         l.GT = take((size_t)l.Vc * l.Np * 2);
         l.comp = take(p->accum == CE_ACC_KAHAN ? (size_t)N * p->D * sizeof(float) : 0);
+        if (p->filter_eps > 0.0f) {
+            const size_t tm = (size_t)(l.Np / 256), tn = (size_t)(l.Vc / 256);
+            l.flags = take(tm * tn * 4 * sizeof(int32_t));
+            l.list_e = take(tm * tn * sizeof(uint16_t));
+            l.cnt_e = take(tm * sizeof(int32_t));
+            l.list_c = take(tn * tm * sizeof(uint16_t));
+            l.cnt_c = take(tn * sizeof(int32_t));
+        }
     }
     l.total = off;
     return l;
@@ -675,7 +686,7 @@ int ce_linear_fwd_bwd(const ce_linear_problem *prob, const void *E, const void *
     fg.target = target;
     fg.col_base = 0;
     fg.stats = stats;
-    VCE_TRY(launch_gemm(fg, GEMM_STATS, ls, s));
+    VCE_TRY(launch_gemm(fg, GEMM_STATS, ls, false, s));
 
     ce_row_final *fin = at<ce_row_final>(ws, l.fin);
     LinMergeArgs ma{stats, (int)l.tiles_v, N, V, target, p.ignore_index, p.label_smoothing,
@@ -691,6 +702,13 @@ int ce_linear_fwd_bwd(const ce_linear_problem *prob, const void *E, const void *
     VCE_TRY(launch_linear_rowconst(ra, s));
     void *G = at<char>(ws, l.G), *GT = at<char>(ws, l.GT);
     float *comp = p.accum == CE_ACC_KAHAN ? at<float>(ws, l.comp) : nullptr;
+    const bool filt = p.filter_eps > 0.0f;
+    const int64_t tiles_tok = l.Np / 256, tiles_chunk = l.Vc / 256;
+    int32_t *flags = filt ? at<int32_t>(ws, l.flags) : nullptr;
+    uint16_t *list_e = filt ? at<uint16_t>(ws, l.list_e) : nullptr;
+    uint16_t *list_c = filt ? at<uint16_t>(ws, l.list_c) : nullptr;
+    int32_t *cnt_e = filt ? at<int32_t>(ws, l.cnt_e) : nullptr;
+    int32_t *cnt_c = filt ? at<int32_t>(ws, l.cnt_c) : nullptr;
     for (int64_t c0 = 0; c0 < V; c0 += l.Vc) {
         const int64_t w = std::min(l.Vc, V - c0), wp = round_up(w, 256);
         GemmArgs gg{};
@@ -708,7 +726,14 @@ int ce_linear_fwd_bwd(const ce_linear_problem *prob, const void *E, const void *
         gg.ldg = wp;
         gg.GT = GT;
         gg.ldgt = l.Np;
-        VCE_TRY(launch_gemm(gg, GEMM_GRAD, ls, s));
+        gg.keep_flags = flags;
+        gg.filter_eps = p.filter_eps;
+        VCE_TRY(launch_gemm(gg, GEMM_GRAD, ls, filt, s));
+        if (filt) {
+            FilterListArgs fl{flags, tiles_tok, wp / 256, list_e, cnt_e, tiles_chunk,
+                              list_c, cnt_c, tiles_tok};
+            VCE_TRY(launch_filter_lists(fl, s));
+        }
 
         GemmArgs cg{}; // dC[c0 .. c0 + w) = G^T E
         cg.A = GT;
@@ -721,7 +746,10 @@ int ce_linear_fwd_bwd(const ce_linear_problem *prob, const void *E, const void *
         cg.tiles_n = (int)(l.Dr / 256);
         cg.out = dC + c0 * D;
         cg.ldo = D;
-        VCE_TRY(launch_gemm(cg, GEMM_STORE, false, s));
+        cg.klist = list_c;
+        cg.kcnt = cnt_c;
+        cg.klist_pitch = tiles_tok;
+        VCE_TRY(launch_gemm(cg, GEMM_STORE, false, filt, s));
 
         GemmArgs eg{}; // dE += G C[c0 .. c0 + w)
         eg.A = G;
@@ -738,7 +766,10 @@ int ce_linear_fwd_bwd(const ce_linear_problem *prob, const void *E, const void *
         eg.ldo = D;
         eg.comp = comp;
         eg.first = c0 == 0;
-        VCE_TRY(launch_gemm(eg, comp ? GEMM_KAHAN : GEMM_ADD, false, s));
+        eg.klist = list_e;
+        eg.kcnt = cnt_e;
+        eg.klist_pitch = tiles_chunk;
+        VCE_TRY(launch_gemm(eg, comp ? GEMM_KAHAN : GEMM_ADD, false, filt, s));
     }
     return CE_OK;
 }

@@ -178,6 +178,27 @@ struct GemmArgs {
     int64_t ldo;
     float *comp;
     int first;
+    // gradient filtering: GEMM_GRAD writes one keep flag per wave and tile
+    // ([tiles_m][tiles_n][4]) for |G| >= filter_eps |k|; the backward
+    // products walk kcnt[tm] K tiles of 256 listed at klist + tm * klist_pitch
+    int32_t *keep_flags;
+    float filter_eps;
+    const uint16_t *klist;
+    const int32_t *kcnt;
+    int64_t klist_pitch;
+};
+
+// lists of kept 256-wide K tiles from the keep flags of one class chunk
+struct FilterListArgs {
+    const int32_t *flags;  // [tiles_m][tiles_n][4]
+    int64_t tiles_m;       // token tiles
+    int64_t tiles_n;       // class tiles of the chunk
+    uint16_t *list_e;      // [tiles_m][pitch_e] kept class tiles of token tile i
+    int32_t *cnt_e;        // [tiles_m]
+    int64_t pitch_e;
+    uint16_t *list_c;      // [tiles_n][pitch_c] kept token tiles of class tile j
+    int32_t *cnt_c;        // [tiles_n]
+    int64_t pitch_c;
 };
 
 struct LinMergeArgs {
@@ -197,7 +218,8 @@ hipError_t launch_linear_merge(const LinMergeArgs &a, hipStream_t stream);
 hipError_t launch_relayout(const RelayoutArgs &a, bool transpose, hipStream_t stream,
                            uint16_t *Yn = nullptr, int64_t Kn = 0);
 hipError_t launch_linear_rowconst(const LinRowArgs &a, hipStream_t stream);
-hipError_t launch_gemm(const GemmArgs &g, int epi, bool ls, hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs &g, int epi, bool ls, bool filt, hipStream_t stream);
+hipError_t launch_filter_lists(const FilterListArgs &a, hipStream_t stream);
 hipError_t launch_zero_f32(float *p, int64_t n, hipStream_t stream);
 
 hipError_t launch_count(const int64_t *target, int64_t T, int64_t ignore_index, int64_t V_total,

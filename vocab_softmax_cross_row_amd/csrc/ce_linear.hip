@@ -182,8 +182,11 @@ __host__ __device__ __forceinline__ int64_t tile_ids(int tiles_m, int tiles_n) {
     return (supers + kXcds - 1) / kXcds * kXcds * kSuperM * kSuperN;
 }
 
-// One 256 x 256 output tile: main loop and epilogue.
-template <int EPI, bool LS>
+// One 256 x 256 output tile: main loop and epilogue.  FILT (gradient
+// filtering): for the G product, record whether the tile keeps any entry;
+// for the backward products, walk only the K tiles listed for this output
+// row tile (the kept 256-wide blocks of G), 4 stages each.
+template <int EPI, bool LS, bool FILT>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, char *lbase) {
     // opaque per tile: values derived from the thread index are not hoisted
     // out of the tile loop, where they would stay live through every tile
@@ -201,8 +204,38 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
         __builtin_amdgcn_make_buffer_rsrc((void *)abase, 0, (int)a_span, 0x00020000);
     const __amdgpu_buffer_rsrc_t rb =
         __builtin_amdgcn_make_buffer_rsrc((void *)bbase, 0, (int)b_span, 0x00020000);
-    const int nk = (int)(g.K / kBK);
+    int nk = (int)(g.K / kBK);
     const int a_kbs = (int)(g.a_ks / 16), b_kbs = (int)(g.b_ks / 16);
+    // the filtered K walk belongs to the backward products only; the G
+    // product with FILT records keep flags and walks all of K
+    constexpr bool kWalk = FILT && (EPI == GEMM_STORE || EPI == GEMM_ADD || EPI == GEMM_KAHAN);
+
+    // Filtered K walk: the kept 256-wide K tiles of this output row tile are
+    // copied into LDS after the two stage buffers (free during the main
+    // loop), and stage kt reads stored stage kstage(kt) = 4 list[kt/4] + kt%4.
+    // km1 / km2 hold kstage(kt + 1) and kstage(kt + 2) while stage kt runs;
+    // each list entry is read from LDS one stage before it is needed.
+    uint16_t *klds = reinterpret_cast<uint16_t *>(lbase + 2 * kStage);
+    if constexpr (kWalk) {
+        nk = 4 * g.kcnt[tm];
+        const uint16_t *src = g.klist + (int64_t)tm * g.klist_pitch;
+        for (int i = tid; i < nk / 4; i += kGT) klds[i] = src[i];
+        __syncthreads();
+        if (nk == 0) {
+            // every K tile dropped: the product is zero; an addition of zero
+            // is skipped, a store (or the first addition) writes zeros
+            if constexpr (EPI == GEMM_ADD || EPI == GEMM_KAHAN) {
+                if (!g.first) return;
+            }
+        }
+    }
+    auto kstage = [&](int kt) -> int {
+        if constexpr (kWalk) {
+            return 4 * __builtin_amdgcn_readfirstlane((int)klds[kt >> 2]) + (kt & 3);
+        } else {
+            return kt;
+        }
+    };
 
     // Wave w owns rows 64w .. 64w+63 of the tile and all 256 columns
     // (2 x 8 accumulators of 32 x 32).  Its A fragments are its own: they go
@@ -222,15 +255,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
     // matters because a bf16 GEMM on this chip runs at a power-limited
     // clock, and moved bytes cost power.
     bf16x8 fa[2][4]; // [row block][K block]
-    auto load_a = [&](int kt, int r, int kb) {
+    // ks: stored stage index (kstage of the loop's stage)
+    auto load_a = [&](int ks, int r, int kb) {
         fa[r][kb] = __builtin_bit_cast(
             bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                        ra, lane * 16, ((2 * wave + r) * a_kbs + g.a_kb0 + kt * 4 + kb) * 1024, 0));
+                        ra, lane * 16, ((2 * wave + r) * a_kbs + g.a_kb0 + ks * 4 + kb) * 1024, 0));
     };
     u32x4 stg[8];
-    auto load_b = [&](int kt, int q) {
+    auto load_b = [&](int ks, int q) {
         stg[q] = __builtin_amdgcn_raw_buffer_load_b128(
-            rb, lane * 16, ((2 * wave + (q >> 2)) * b_kbs + g.b_kb0 + kt * 4 + (q & 3)) * 1024, 0);
+            rb, lane * 16, ((2 * wave + (q >> 2)) * b_kbs + g.b_kb0 + ks * 4 + (q & 3)) * 1024, 0);
     };
     auto write_b = [&](int buf, int q) {
         *reinterpret_cast<u32x4 *>(lbase + buf * kStage + ((2 * wave + (q >> 2)) * 4 + (q & 3)) * 1024 +
@@ -243,19 +277,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
         for (int j = 0; j < 8; ++j)
             fb[set][j] = *reinterpret_cast<const bf16x8 *>(st + (j * 4 + kb) * 1024 + lane * 16);
     };
-#pragma unroll
-    for (int q = 0; q < 8; ++q) load_b(0, q);
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) load_a(0, r, kb);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) write_b(0, q);
-    if (nk > 1) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) load_b(1, q);
-    }
-
     f32x16 acc[2][8];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -263,6 +284,26 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
         for (int j = 0; j < 8; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    int km1 = 1, km2 = 2;
+    if (nk > 0) {
+    const int k0 = kstage(0);
+    if constexpr (kWalk) {
+        km1 = kstage(1);
+        km2 = kstage(2);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) load_b(k0, q);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) load_a(k0, r, kb);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) write_b(0, q);
+    if (nk > 1) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) load_b(km1, q);
+    }
+
     __syncthreads();
     read_b(0, 0, 0);
 
@@ -274,6 +315,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
     auto run_stage = [&](int kt, auto MORE1, auto MORE2) {
         constexpr bool more1 = decltype(MORE1)::value, more2 = decltype(MORE2)::value;
         const int cb = kt & 1, nb = cb ^ 1;
+        // stored stage indices of stages kt + 1 and kt + 2
+        const int s1 = kWalk ? km1 : kt + 1, s2 = kWalk ? km2 : kt + 2;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const int cur = kb & 1;
@@ -286,7 +329,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
 #pragma unroll
                 for (int q = q_lo[kb]; q < q_lo[kb + 1]; ++q) {
                     if constexpr (more1) write_b(nb, q);
-                    if constexpr (more2) load_b(kt + 2, q);
+                    if constexpr (more2) load_b(s2, q);
                 }
             }
 #pragma unroll
@@ -296,8 +339,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][kb], fb[cur][j],
                                                                          acc[i][j], 0, 0, 0);
             if constexpr (more1) {
-                load_a(kt + 1, 0, kb);
-                load_a(kt + 1, 1, kb);
+                load_a(s1, 0, kb);
+                load_a(s1, 1, kb);
             }
             // issue order: MFMA, LDS read (x8); MFMA, LDS write, B load;
             // MFMA, the two A loads
@@ -323,6 +366,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
             __builtin_amdgcn_sched_barrier(0);
             if (kb == 2) __syncthreads();
         }
+        if constexpr (kWalk) {
+            // the next stage's pair (stage kt + 3 read from the list now)
+            km1 = km2;
+            if (kt + 3 < nk) km2 = kstage(kt + 3);
+        }
     };
     using Yes = std::true_type;
     using No = std::false_type;
@@ -335,6 +383,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
     }
     if (nk >= 2) run_stage(nk - 2, Yes{}, No{});
     run_stage(nk - 1, No{}, No{});
+    } // nk > 0
     // Every accumulator is pinned here.  MFMAs touch no memory, so a barrier
     // alone does not keep them above the epilogue: the compiler has sunk the
     // last ones into the epilogue, among its LDS writes of accumulators, and
@@ -495,6 +544,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
         }
         char *GT = reinterpret_cast<char *>(g.GT);
         char *G = reinterpret_cast<char *>(g.G);
+        // gradient filtering: whether this lane saw an entry of a valid row
+        // with |G| >= filter_eps |k| (|p - q| >= filter_eps unscaled)
+        bool kept = false;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             __syncthreads();
@@ -519,6 +571,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
                     if (R.valid && v < g.N)
                         x = (v == tcl) ? R.c.gk : grad_elem<CE_BF16, LS>(z, R.c);
                     gv[e] = x;
+                }
+                if constexpr (FILT) {
+                    const float thr = g.filter_eps * fabsf(R.c.k);
+                    float mx = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(gv[e]));
+                    kept = kept || (R.valid && mx >= thr);
                 }
                 u32x4 w;
 #pragma unroll
@@ -545,6 +604,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
                                     (int64_t)((v & 31) + 32 * ((n0 & 15) >> 3)) * 16;
                 *reinterpret_cast<u32x4 *>(GT + off) = w;
             }
+        }
+        if constexpr (FILT) {
+            // one flag per wave (its 64 rows of the tile); the list kernel ORs them
+            const bool any = __builtin_amdgcn_ballot_w64(kept) != 0;
+            if (lane == 0)
+                g.keep_flags[((int64_t)tm * g.tiles_n + tn) * 4 + wave] = any ? 1 : 0;
         }
     } else {
         // plain fp32 result: store, add, or add with Kahan compensation;
@@ -609,21 +674,49 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
 template <int EPI>
 constexpr bool kGemmPersistent = EPI != GEMM_GRAD;
 
-template <int EPI, bool LS>
+template <int EPI, bool LS, bool FILT>
 __global__ __launch_bounds__(kGT) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_gemm(GemmArgs g) {
     extern __shared__ __attribute__((aligned(16))) u32x4 lds[];
     char *lbase = reinterpret_cast<char *>(lds);
     int tm, tn;
     if constexpr (!kGemmPersistent<EPI>) {
-        if (tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn)) gemm_tile<EPI, LS>(g, tm, tn, lbase);
+        if (tile_of(blockIdx.x, g.tiles_m, g.tiles_n, tm, tn))
+            gemm_tile<EPI, LS, FILT>(g, tm, tn, lbase);
         return;
     }
     const int64_t ids = tile_ids(g.tiles_m, g.tiles_n);
     for (int64_t b = blockIdx.x; b < ids; b += gridDim.x) {
         if (!tile_of(b, g.tiles_m, g.tiles_n, tm, tn)) continue;
-        gemm_tile<EPI, LS>(g, tm, tn, lbase);
+        gemm_tile<EPI, LS, FILT>(g, tm, tn, lbase);
         __syncthreads(); // the epilogue's LDS is the next tile's stage buffers
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Gradient filtering: from the G product's per-wave keep flags of one class
+// chunk ([tiles_m][tiles_n][4]), the kept K tiles of each backward output
+// row tile, in increasing order: for dE (row tile = token tile i) the kept
+// class tiles j, for dC (row tile = class tile j) the kept token tiles i.
+// One thread per list.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_filter_lists(FilterListArgs a) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    auto keep = [&](int64_t i, int64_t j) {
+        const int32_t *f = a.flags + (i * a.tiles_n + j) * 4;
+        return (f[0] | f[1] | f[2] | f[3]) != 0;
+    };
+    if (t < a.tiles_m) {
+        int c = 0;
+        for (int64_t j = 0; j < a.tiles_n; ++j)
+            if (keep(t, j)) a.list_e[t * a.pitch_e + c++] = (uint16_t)j;
+        a.cnt_e[t] = c;
+    } else if (t < a.tiles_m + a.tiles_n) {
+        const int64_t j = t - a.tiles_m;
+        int c = 0;
+        for (int64_t i = 0; i < a.tiles_m; ++i)
+            if (keep(i, j)) a.list_c[j * a.pitch_c + c++] = (uint16_t)i;
+        a.cnt_c[j] = c;
     }
 }
 
@@ -726,11 +819,11 @@ hipError_t launch_linear_rowconst(const LinRowArgs &a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int EPI, bool LS>
+template <int EPI, bool LS, bool FILT = false>
 static hipError_t gemm_launch(const GemmArgs &g, hipStream_t stream) {
     static std::atomic<bool> attr[kMaxDevices];
     static std::atomic<int> slot_cache[kMaxDevices];
-    const void *kern = (const void *)k_gemm<EPI, LS>;
+    const void *kern = (const void *)k_gemm<EPI, LS, FILT>;
     hipError_t e = raise_lds_once(kern, kGemmLdsBytes, attr);
     if (e != hipSuccess) return e;
     // as many workgroups as the device holds at once, a multiple of 8
@@ -740,11 +833,23 @@ static hipError_t gemm_launch(const GemmArgs &g, hipStream_t stream) {
     const int64_t ids = tile_ids(g.tiles_m, g.tiles_n);
     const int64_t slots = std::max<int64_t>(kXcds, held / kXcds * kXcds);
     const dim3 grid((unsigned)(kGemmPersistent<EPI> ? std::min(ids, slots) : ids));
-    hipLaunchKernelGGL((k_gemm<EPI, LS>), grid, dim3(kGT), kGemmLdsBytes, stream, g);
+    hipLaunchKernelGGL((k_gemm<EPI, LS, FILT>), grid, dim3(kGT), kGemmLdsBytes, stream, g);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmArgs &g, int epi, bool ls, hipStream_t stream) {
+hipError_t launch_gemm(const GemmArgs &g, int epi, bool ls, bool filt, hipStream_t stream) {
+    if (filt) {
+        // the filtered kernels dereference their filtering buffers
+        if (epi == GEMM_GRAD ? !g.keep_flags : (!g.klist || !g.kcnt)) return hipErrorInvalidValue;
+        switch (epi) {
+        case GEMM_GRAD: return ls ? gemm_launch<GEMM_GRAD, true, true>(g, stream)
+                                  : gemm_launch<GEMM_GRAD, false, true>(g, stream);
+        case GEMM_STORE: return gemm_launch<GEMM_STORE, false, true>(g, stream);
+        case GEMM_ADD: return gemm_launch<GEMM_ADD, false, true>(g, stream);
+        case GEMM_KAHAN: return gemm_launch<GEMM_KAHAN, false, true>(g, stream);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (epi) {
     case GEMM_STATS: return ls ? gemm_launch<GEMM_STATS, true>(g, stream)
                                : gemm_launch<GEMM_STATS, false>(g, stream);
@@ -755,6 +860,12 @@ hipError_t launch_gemm(const GemmArgs &g, int epi, bool ls, hipStream_t stream) 
     case GEMM_KAHAN: return gemm_launch<GEMM_KAHAN, false>(g, stream);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_filter_lists(const FilterListArgs &a, hipStream_t stream) {
+    const int64_t n = a.tiles_m + a.tiles_n;
+    hipLaunchKernelGGL(k_filter_lists, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 } // namespace vce
