@@ -257,10 +257,12 @@ int ce_fused_fwd_bwd_noalloc(const ce_problem *prob, const void *logits, int log
  *   operand of the two backward products;
  *   dE = G C   [N, D] fp32,  dC = G^T E  [V, D] fp32.
  *
- * The vocabulary is processed in chunks of CE_LINEAR_CHUNK classes: dC rows
- * of a chunk are complete after it, dE is summed over the chunks in fp32 or,
- * with CE_ACC_KAHAN, with a Kahan compensation term (one more [N, D] fp32
- * workspace buffer).  Everything is deterministic (no atomics). */
+ * The backward processes the vocabulary in chunks of at most
+ * CE_LINEAR_CHUNK classes, fewer when the chunk's bf16 G and G^T would pass
+ * 256 MiB (8192 classes at 8192 tokens): dC rows of a chunk are complete
+ * after it, dE is summed over the chunks in fp32 or, with CE_ACC_KAHAN,
+ * with a Kahan compensation term (one more [N, D] fp32 workspace buffer).
+ * Everything is deterministic (no atomics). */
 #define CE_LINEAR_CHUNK 16384
 
 typedef enum {

@@ -222,7 +222,11 @@ LinLayout linear_layout(const ce_linear_problem *p, bool backward) {
     l.Dp = round_up(p->D, 64);
     l.Dr = round_up(p->D, 256);
     l.Vp = round_up(p->V, 256);
-    l.Vc = std::min<int64_t>(CE_LINEAR_CHUNK, l.Vp);
+    // classes per backward chunk: CE_LINEAR_CHUNK, fewer when one chunk's G
+    // and G^T (4 Np Vc bytes) would pass kLinGBudget
+    const int64_t fit = kLinGBudget / (4 * l.Np) / 256 * 256;
+    l.Vc = std::min<int64_t>(std::min<int64_t>(CE_LINEAR_CHUNK, l.Vp),
+                             std::max<int64_t>(256, fit));
     l.tiles_v = l.Vp / 256;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -232,13 +236,13 @@ LinLayout linear_layout(const ce_linear_problem *p, bool backward) {
     };
     l.Ef = take((size_t)l.Np * l.Dp * 2);
     l.Cf = take((size_t)l.Vp * l.Dp * 2);
-    l.stats = take((size_t)l.tiles_v * N * sizeof(ce_row_stats));
+    l.stats = take((size_t)l.tiles_v * N * sizeof(LinTileStats));
     l.fin = take((size_t)N * sizeof(ce_row_final));
     l.loss_rows = take((size_t)N * sizeof(float));
     l.counts = take(2 * sizeof(int32_t));
     if (backward) {
         l.ETf = take((size_t)l.Dr * l.Np * 2);
-        l.CTf = take((size_t)l.Dr * l.Vp * 2);
+        l.CTf = take((size_t)l.Dr * l.Vc * 2); // C^T of one chunk
         l.rows = take((size_t)N * kLinRowBytes);
         l.G = take((size_t)l.Np * l.Vc * 2);
         l.GT = take((size_t)l.Vc * l.Np * 2);
@@ -663,17 +667,16 @@ int ce_linear_fwd_bwd(const ce_linear_problem *prob, const void *E, const void *
     uint16_t *ETf = bwd ? at<uint16_t>(ws, l.ETf) : nullptr;
     uint16_t *CTf = bwd ? at<uint16_t>(ws, l.CTf) : nullptr;
     if (bwd) {
-        // both operand forms of E and of C from one read of each
+        // both operand forms of E from one read; C^T is formed per chunk below
         VCE_TRY(launch_relayout(RelayoutArgs{Eh, N, D, D, ETf, l.Dr, l.Np}, true, s, Ef, l.Dp));
-        VCE_TRY(launch_relayout(RelayoutArgs{Ch, V, D, D, CTf, l.Dr, l.Vp}, true, s, Cf, l.Dp));
     } else {
         VCE_TRY(launch_relayout(RelayoutArgs{Eh, N, D, D, Ef, l.Np, l.Dp}, false, s));
-        VCE_TRY(launch_relayout(RelayoutArgs{Ch, V, D, D, Cf, l.Vp, l.Dp}, false, s));
     }
+    VCE_TRY(launch_relayout(RelayoutArgs{Ch, V, D, D, Cf, l.Vp, l.Dp}, false, s));
 
     // forward: per (256-class tile, row) statistics of the logits, merged
     const bool ls = p.label_smoothing > 0.0f;
-    ce_row_stats *stats = at<ce_row_stats>(ws, l.stats);
+    LinTileStats *stats = at<LinTileStats>(ws, l.stats);
     GemmArgs fg{};
     fg.A = Ef;
     fg.B = Cf;
@@ -751,12 +754,14 @@ int ce_linear_fwd_bwd(const ce_linear_problem *prob, const void *E, const void *
         cg.klist_pitch = tiles_tok;
         VCE_TRY(launch_gemm(cg, GEMM_STORE, false, filt, s));
 
+        // C^T of this chunk's classes, fragment-major (rows D, K the classes)
+        VCE_TRY(launch_relayout(RelayoutArgs{Ch + c0 * D, w, D, D, CTf, l.Dr, wp}, true, s));
         GemmArgs eg{}; // dE += G C[c0 .. c0 + w)
         eg.A = G;
         eg.B = CTf;
         eg.a_ks = wp;
-        eg.b_ks = l.Vp;
-        eg.b_kb0 = (int)(c0 / 16);
+        eg.b_ks = wp;
+        eg.b_kb0 = 0;
         eg.K = wp;
         eg.M = N;
         eg.N = D;

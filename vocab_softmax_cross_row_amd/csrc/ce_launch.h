@@ -132,6 +132,9 @@ struct GradArgs {
 
 // ---- linear classifier (ce_linear.hip) ------------------------------------
 constexpr int kLinRowBytes = 48;         // per-row gradient constants
+// bytes one backward chunk's G and G^T may take (the chunk is narrowed for
+// many tokens: at 8192 tokens, 8192 classes)
+constexpr int64_t kLinGBudget = (int64_t)256 << 20;
 constexpr int kGemmLdsBytes = 147456;    // 144 KB of the CU's 160 KB
 enum { GEMM_STATS = 0, GEMM_GRAD = 1, GEMM_STORE = 2, GEMM_ADD = 3, GEMM_KAHAN = 4 };
 
@@ -155,6 +158,14 @@ struct LinRowArgs {
     void *rows; // [N] x kLinRowBytes
 };
 
+// Statistics of one row over one 256-class tile of the linear classifier's
+// logits (fp32, as computed): non-target max m, sum of exp(z - m) over the
+// non-target columns, the target logit if the tile holds the target column
+// (else 0), and the sum of all its logits (label smoothing; else 0).
+struct LinTileStats {
+    float m, s, zt, sz;
+};
+
 // out[M, N] = A[M, K] B[N, K]^T, A and B fragment-major bf16
 struct GemmArgs {
     const void *A, *B;
@@ -166,7 +177,7 @@ struct GemmArgs {
     // GEMM_STATS
     const int64_t *target;
     int64_t col_base;   // class of output column 0
-    ce_row_stats *stats; // [M][tiles_n]
+    LinTileStats *stats; // [M][tiles_n]
     // GEMM_GRAD
     const void *rows;   // per-row constants [M]
     void *G;            // fragment-major, rows = tokens, K = classes (ldg)
@@ -202,7 +213,7 @@ struct FilterListArgs {
 };
 
 struct LinMergeArgs {
-    const ce_row_stats *stats; // [N][S]
+    const LinTileStats *stats; // [N][S]
     int S;
     int64_t N, V;
     const int64_t *target;

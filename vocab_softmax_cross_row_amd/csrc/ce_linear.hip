@@ -429,7 +429,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
         float *ps = reinterpret_cast<float *>(ex + 3072);
         float *pz = reinterpret_cast<float *>(ex + 5120);
         float *zt = reinterpret_cast<float *>(ex + 7168);         // [256]
-        int32_t *own = reinterpret_cast<int32_t *>(ex + 8192);    // [256]
         {
             const int64_t r = row0 + tid;
             int32_t tl = -1;
@@ -439,7 +438,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
             }
             t_l[tid] = tl;
             zt[tid] = 0.0f;
-            own[tid] = 0;
         }
         // one row-pass step: 8 columns of one row per lane, reduced over the
         // row's 16 lanes; FULL: every column of the tile is inside N
@@ -462,7 +460,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
 #pragma unroll
                 for (int q = 1; q < 8; ++q) v = (q == d) ? z[q] : v;
                 zt[row] = v;
-                own[row] = 1;
             }
             float mx = ninf(), sz = 0.0f;
 #pragma unroll
@@ -508,13 +505,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
             double s = 0.0;
             if (m0 != ninf()) s += (double)ps[tid] * exp_nonpos((double)m0 - (double)M);
             if (m1 != ninf()) s += (double)ps[256 + tid] * exp_nonpos((double)m1 - (double)M);
-            ce_row_stats o;
+            LinTileStats o;
             o.m = M;
+            o.s = (float)s;
             o.zt = zt[tid];
-            o.own = own[tid];
-            o.reserved = 0;
-            o.s = s;
-            o.sz = LS ? (double)pz[tid] + (double)pz[256 + tid] : 0.0;
+            o.sz = LS ? (float)((double)pz[tid] + (double)pz[256 + tid]) : 0.0f;
             g.stats[r * g.tiles_n + tn] = o;
         }
     } else if constexpr (EPI == GEMM_GRAD) {
@@ -732,30 +727,29 @@ __global__ __launch_bounds__(kMergeWaves * kWave) void k_linear_merge(LinMergeAr
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t r = (int64_t)blockIdx.x * kMergeWaves + (threadIdx.x >> 6);
     if (r >= a.N) return;
-    const ce_row_stats *in = a.stats + r * a.S;
+    const LinTileStats *in = a.stats + r * a.S;
     float m = ninf();
     for (int k = lane; k < a.S; k += kWave) m = fmaxf(m, in[k].m);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, kWave));
     const double M = (double)m;
     double s = 0.0, zt = 0.0, sz = 0.0;
-    int own = 0;
     for (int k = lane; k < a.S; k += kWave) {
-        const ce_row_stats p = in[k];
-        if (p.m != ninf()) s += p.s * exp((double)p.m - M);
-        zt += (double)p.zt;
-        own += p.own;
-        sz += p.sz;
+        const LinTileStats p = in[k];
+        if (p.m != ninf()) s += (double)p.s * exp((double)p.m - M);
+        zt += (double)p.zt; // 0 except in the tile that holds the target
+        sz += (double)p.sz;
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         s += __shfl_xor(s, o, kWave);
         zt += __shfl_xor(zt, o, kWave);
         sz += __shfl_xor(sz, o, kWave);
-        own += __shfl_xor(own, o, kWave);
     }
     if (lane != 0) return;
     const int64_t t = a.target[r];
+    // a target in [0, V) lies in exactly one tile, which recorded its logit
+    const int own = (t >= 0 && t < a.V) ? 1 : 0;
     ce_row_final fo;
     fo.lse = 0.0;
     fo.gt = 0.0;
