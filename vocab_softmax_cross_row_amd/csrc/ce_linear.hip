@@ -693,25 +693,37 @@ void k_gemm(GemmArgs g) {
 // chunk ([tiles_m][tiles_n][4]), the kept K tiles of each backward output
 // row tile, in increasing order: for dE (row tile = token tile i) the kept
 // class tiles j, for dC (row tile = class tile j) the kept token tiles i.
-// One thread per list.
+// One wave per list: 64 candidates at a time, a ballot, and each kept one
+// written at its rank among the kept lanes below it.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_filter_lists(FilterListArgs a) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+constexpr int kListWaves = 4;
+
+__global__ __launch_bounds__(kListWaves * kWave) void k_filter_lists(FilterListArgs a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t w = (int64_t)blockIdx.x * kListWaves + (threadIdx.x >> 6);
     auto keep = [&](int64_t i, int64_t j) {
-        const int32_t *f = a.flags + (i * a.tiles_n + j) * 4;
-        return (f[0] | f[1] | f[2] | f[3]) != 0;
+        const u32x4 f = *reinterpret_cast<const u32x4 *>(a.flags + (i * a.tiles_n + j) * 4);
+        return (f[0] | f[1] | f[2] | f[3]) != 0u;
     };
-    if (t < a.tiles_m) {
-        int c = 0;
-        for (int64_t j = 0; j < a.tiles_n; ++j)
-            if (keep(t, j)) a.list_e[t * a.pitch_e + c++] = (uint16_t)j;
-        a.cnt_e[t] = c;
-    } else if (t < a.tiles_m + a.tiles_n) {
-        const int64_t j = t - a.tiles_m;
-        int c = 0;
-        for (int64_t i = 0; i < a.tiles_m; ++i)
-            if (keep(i, j)) a.list_c[j * a.pitch_c + c++] = (uint16_t)i;
-        a.cnt_c[j] = c;
+    const bool for_e = w < a.tiles_m;
+    if (!for_e && w >= a.tiles_m + a.tiles_n) return;
+    const int64_t n = for_e ? a.tiles_n : a.tiles_m;        // candidates of this list
+    uint16_t *out = for_e ? a.list_e + w * a.pitch_e : a.list_c + (w - a.tiles_m) * a.pitch_c;
+    int c = 0;
+    for (int64_t base = 0; base < n; base += kWave) {
+        const int64_t x = base + lane;
+        const bool k = x < n && (for_e ? keep(w, x) : keep(x, w - a.tiles_m));
+        const uint64_t b = __builtin_amdgcn_ballot_w64(k);
+        const int rank = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+        if (k) out[c + rank] = (uint16_t)x;
+        c += __builtin_popcountll(b);
+    }
+    if (lane == 0) {
+        if (for_e)
+            a.cnt_e[w] = c;
+        else
+            a.cnt_c[w - a.tiles_m] = c;
     }
 }
 
@@ -857,8 +869,9 @@ hipError_t launch_gemm(const GemmArgs &g, int epi, bool ls, bool filt, hipStream
 }
 
 hipError_t launch_filter_lists(const FilterListArgs &a, hipStream_t stream) {
-    const int64_t n = a.tiles_m + a.tiles_n;
-    hipLaunchKernelGGL(k_filter_lists, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+    const int64_t n = a.tiles_m + a.tiles_n; // one wave per list
+    hipLaunchKernelGGL(k_filter_lists, dim3((unsigned)((n + kListWaves - 1) / kListWaves)),
+                       dim3(kListWaves * kWave), 0, stream, a);
     return hipGetLastError();
 }
 
