@@ -286,9 +286,10 @@ typedef struct {
  * that off -- the page does not state the rule; this is the reading taken):
  * the unscaled gradient u = softmax(z) - q (G = k u, target entries from
  * the 1/4 select) is cut into blocks of 256 tokens x 256 classes aligned at
- * token 0 and class 0; a block in which every entry of every valid row has
- * |u| < filter_eps is dropped -- taken as zero in both backward products,
- * whose work for it is skipped.  The loss is exact either way.  2^-8 (the
+ * token 0 and class 0; a block in which every entry of every valid row with
+ * k_r != 0 has |u| < filter_eps is dropped -- taken as zero in both backward
+ * products, whose work for it is skipped.  (A row with k_r = 0, e.g. a zero
+ * per-row grad_output, has an all-zero gradient and keeps no block.)  The loss is exact either way.  2^-8 (the
  * bf16 unit roundoff) drops blocks whose entries all vanish next to a unit
  * entry at bf16 resolution.  The error this brings into an entry of dE or
  * dC is at most the sum over the dropped blocks' entries of |G| times the

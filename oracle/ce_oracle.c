@@ -460,12 +460,14 @@ void oracle_linear_forward(const void *E, const void *C, int dtype, int64_t n, i
  * u_rv = d loss_r / d z_rv (softmax minus the smoothed one-hot, the target
  * entry -sigma(x) + eps (V-1)/V) is cut into blocks of 256 rows x 256
  * classes, block (i, j) holding rows 256 i .. 256 i + 255 and classes
- * 256 j .. 256 j + 255 (the last ones ragged); with tau > 0 a block whose
- * every |u_rv| is below tau is dropped: its G entries are taken as zero in
- * both contractions.  tau <= 0 keeps every block (the exact gradients).
+ * 256 j .. 256 j + 255 (the last ones ragged); with tau > 0 a block is
+ * dropped when |u_rv| < tau for every row r of the block whose gradient is
+ * not identically zero (status 1 and k_r != 0): its G entries are taken as
+ * zero in both contractions.  tau <= 0 keeps every block (the exact
+ * gradients).
  *   keep      [ceil(n/256), ceil(V/256)] int32, 1 kept / 0 dropped (may be NULL)
- *   block_max same shape, fp64: max |u_rv| over the block (0 for blocks of
- *             rows whose status is not 1) (may be NULL) */
+ *   block_max same shape, fp64: max |u_rv| over those rows of the block (0
+ *             when there are none) (may be NULL) */
 void oracle_linear_backward(const void *E, const void *C, int dtype, int64_t n, int64_t D,
                             int64_t V, const int64_t *target, const int32_t *status,
                             const double *x, const double *lse, double eps, const double *k,
@@ -495,9 +497,12 @@ void oracle_linear_backward(const void *E, const void *C, int dtype, int64_t n, 
     for (int64_t bi = 0; bi < nbr; ++bi) {
         for (int64_t bj = 0; bj < nbv; ++bj) {
             double m = 0.0;
-            for (int64_t r = bi * B; r < n && r < (bi + 1) * B; ++r)
+            for (int64_t r = bi * B; r < n && r < (bi + 1) * B; ++r) {
+                if (status[r] != 1 || k[r] == 0.0)
+                    continue; /* an all-zero gradient row keeps no block */
                 for (int64_t v = bj * B; v < V && v < (bj + 1) * B; ++v)
                     m = fmax(m, fabs(G[(size_t)r * (size_t)V + v]));
+            }
             kp[bi * nbv + bj] = (tau <= 0.0) || (m >= tau);
             if (keep) keep[bi * nbv + bj] = kp[bi * nbv + bj];
             if (block_max) block_max[bi * nbv + bj] = m;

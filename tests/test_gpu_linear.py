@@ -323,3 +323,28 @@ def test_filtering_full_workload_one_token_tile():
     assert_loss_rows(out["loss_rows"][rows], {"loss_rows": fref["loss_rows"],
                                               "status": fref["status"]}, "filtered full")
     assert_linear_grad_close(out["dE"][rows], fref["dE"], fref["rsE"], "filtered full dE")
+
+
+def test_filtering_with_per_row_grad_output():
+    """reduction none with per-row weights (some zero, some negative): a
+    row's threshold scales with |k_r|, so the decisions are those of the
+    unscaled gradient; dE and dC against the filtered oracle."""
+    case = _case(300, 128, B.CE_LINEAR_CHUNK + 500, 2123, reduction="none")
+    E, C, t = S.generate_linear(case, device=DEV)
+    t = _targets_in(t, [(0, 700), (16500, 16884)], 2124)
+    go = torch.linspace(-1.5, 2.0, 300, device=DEV)
+    go[::7] = 0.0
+    out = vce.linear_cross_entropy(E, C, t, reduction="none", grad_output=go, filter_eps=TAU)
+    torch.cuda.synchronize()
+    Eb = E.cpu().view(torch.int16).numpy().view(np.uint16)
+    Cb = C.cpu().view(torch.int16).numpy().view(np.uint16)
+    from oracle import ce_oracle as O
+    fref = O.linear_fwd_bwd(Eb, Cb, t.cpu().numpy(), reduction="none",
+                            grad_output=go.cpu().double().numpy(), filter_eps=TAU)
+    bm = fref["block_max"]
+    assert np.all((bm < TAU / 2) | (bm > 2 * TAU)), "a block decision too close to the threshold"
+    assert fref["keep"].any() and not fref["keep"].all()
+    assert_loss_rows(out["loss_rows"], {"loss_rows": fref["loss_rows"], "status": fref["status"]},
+                     "filtered none")
+    assert_linear_grad_close(out["dE"], fref["dE"], fref["rsE"], "filtered none dE")
+    assert_linear_grad_close(out["dC"], fref["dC"], fref["rsC"], "filtered none dC")

@@ -209,3 +209,43 @@ def test_gradient_filtering_limits():
     assert np.all(big["keep"] == 0)
     assert np.all(big["dE"] == 0.0) and np.all(big["dC"] == 0.0)
     assert np.array_equal(big["loss_rows"], ex["loss_rows"])
+
+
+def test_gradient_filtering_with_per_row_weights():
+    """reduction none with per-row weights, some zero and some negative: the
+    unscaled gradient of a row is its autograd gradient divided by its
+    weight, and a row of weight zero (an all-zero gradient) keeps no block.
+    Every row of block row 0 except those of weight zero has targets in class
+    block 0 only, so with the zero-weight rows voting, block (0, 1) would be
+    kept by the target of a zero-weight row placed there."""
+    tau = 2.0 ** -7
+    E, C, t = _filter_case(7)
+    n = len(t)
+    go = np.linspace(-1.5, 2.0, n)
+    go[::5] = 0.0
+    t[10] = 300                       # a zero-weight row (10 % 5 == 0) targets class block 1
+    o = O.linear_fwd_bwd(E, C, t, reduction="none", grad_output=go, filter_eps=tau)
+    z = torch.tensor(E @ C.T, requires_grad=True)
+    loss = torch.nn.functional.cross_entropy(z, torch.tensor(t), ignore_index=-100,
+                                             reduction="none")
+    loss.backward(torch.tensor(go))
+    G = z.grad.numpy()
+    vote = (go != 0.0) & (t != -100)
+    U = np.zeros_like(G)
+    U[vote] = np.abs(G[vote] / go[vote, None])
+    bm = np.zeros((2, 3))
+    for i in range(2):
+        for j in range(3):
+            bm[i, j] = U[256 * i:256 * (i + 1), 256 * j:256 * (j + 1)].max()
+    keep = bm >= tau
+    assert not keep[0, 1], "the zero-weight row must not keep block (0, 1)"
+    assert np.all((bm < tau / 2) | (bm > 2 * tau))
+    assert np.allclose(o["block_max"], bm, rtol=1e-12, atol=1e-15)
+    assert np.array_equal(o["keep"], keep.astype(np.int32))
+    Gf = G.copy()
+    for i in range(2):
+        for j in range(3):
+            if not keep[i, j]:
+                Gf[256 * i:256 * (i + 1), 256 * j:256 * (j + 1)] = 0.0
+    assert np.allclose(o["dE"], Gf @ C, rtol=1e-10, atol=1e-15)
+    assert np.allclose(o["dC"], Gf.T @ E, rtol=1e-10, atol=1e-15)

@@ -540,7 +540,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
         char *GT = reinterpret_cast<char *>(g.GT);
         char *G = reinterpret_cast<char *>(g.G);
         // gradient filtering: whether this lane saw an entry of a valid row
-        // with |G| >= filter_eps |k| (|p - q| >= filter_eps unscaled)
+        // with k != 0 and |G| >= filter_eps |k| (|p - q| >= filter_eps
+        // unscaled); a row with k = 0 has an all-zero gradient and keeps
+        // nothing
         bool kept = false;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -572,7 +574,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
                     float mx = 0.0f;
 #pragma unroll
                     for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(gv[e]));
-                    kept = kept || (R.valid && mx >= thr);
+                    kept = kept || (R.valid && R.c.k != 0.0f && mx >= thr);
                 }
                 u32x4 w;
 #pragma unroll
