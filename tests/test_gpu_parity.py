@@ -4,6 +4,7 @@ Sizes the oracle finishes in seconds but that span several vectors per
 thread, several workgroup shapes, a scalar tail and the split-V grid; every
 case is seeded (synth/ce_inputs.py).  Tolerances: tests/parity_util.py.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -902,3 +903,86 @@ def test_single_row(V, dt, eps):
     ref = P.oracle_for(logits, target, eps=eps)
     P.assert_loss_rows(f["loss_rows"], ref, "T=1 unfused")
     P.assert_grad_close(g, ref["grad"], "T=1 unfused grad")
+
+
+# --------------------------------------------------------------------------
+# small batches: row tails inside aligned rows, the most rows of a short
+# width, per-row weights, a single row
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("in_dt,out_dt,T,V,ld,reduction", [
+    (torch.float32, torch.float32, 64, 1000, 1000, "mean"),    # the tiny workload's shape
+    (torch.bfloat16, torch.bfloat16, 300, 1003, 1008, "mean"),  # a 3-logit tail per row
+    (torch.bfloat16, torch.float32, 1024, 120, 120, "sum"),
+    (torch.float32, torch.bfloat16, 33, 2048, 2048, "none"),    # 8 vectors per lane
+    (torch.bfloat16, torch.bfloat16, 1, 64, 64, "mean"),
+    (torch.bfloat16, torch.bfloat16, 1025, 120, 120, "mean"),
+])
+def test_small_batch_single_launch(in_dt, out_dt, T, V, ld, reduction):
+    """Small batches with the gradient rows at the logits' stride (so a
+    short tail sits inside 16-byte aligned rows): every output against the
+    oracle, including ignored rows, a confident row and per-row weights."""
+    base = S.TINY if in_dt == torch.float32 else S.MID
+    c = S.scaled(base, T, ld, 930 + T, dtype=in_dt, reduction=reduction)
+    full, target = S.generate(c)
+    logits = full.to(DEV)[:, :V]
+    target = target.clamp(max=V - 1)
+    target[target < 0] = -100
+    target = target.to(DEV)
+    if T > 2:
+        target[1] = -100
+        logits[2, int(target[2]) if int(target[2]) >= 0 else 0] = 30.0   # a confident row
+    go = None
+    if reduction == "none":
+        go = torch.linspace(-1.0, 2.0, T, device=DEV)
+    elif reduction == "sum":
+        go = torch.tensor([0.5], device=DEV)
+    what = f"small {in_dt}->{out_dt} {T}x{V}"
+    _say(f"[small] {what} ld={ld} {reduction}")
+    # the gradient rows share the logits' stride, so both stay 16-byte aligned
+    grad = torch.empty((T, ld), dtype=out_dt, device=DEV)[:, :V]
+    out = vce.fused_fwd_bwd(logits, target, reduction=reduction, grad_output=go, grad=grad)
+    torch.cuda.synchronize()
+    ref = P.oracle_for(logits, target, reduction=reduction,
+                       grad_output=1.0 if go is None else go)
+    assert int(out["n_valid"].item()) == ref["n_valid"]
+    assert int(out["err_count"].item()) == ref["n_bad"]
+    P.assert_loss_rows(out["loss_rows"], ref, what)
+    if reduction != "none":
+        P.assert_scalar_loss(out["loss"].item(), ref["loss"], what)
+    P.assert_grad_close(out["grad"], ref["grad"], what)
+    P.assert_collapse_rows(out["loss_rows"], out["grad"].cpu(), target.cpu(), ref,
+                           P.collapse_rows(logits, target), what)
+
+
+def test_small_batch_edge_rows():
+    """Small batches: bad targets, an all-ignored batch (mean NaN), -inf
+    logits and an in-place gradient."""
+    logits = torch.randn((8, 512), device=DEV)
+    target = torch.tensor([0, 1, 512, -1, -100, 7, 10**12, 3], dtype=torch.int64, device=DEV)
+    out = vce.fused_fwd_bwd(logits, target, reduction="sum")
+    torch.cuda.synchronize()
+    assert out["err_count"].item() == 3 and out["n_valid"].item() == 4
+    lr = out["loss_rows"].cpu()
+    assert torch.isnan(lr[[2, 3, 6]]).all() and lr[4].item() == 0.0
+    assert torch.all(out["grad"][[2, 3, 4, 6]] == 0) and math.isnan(out["loss"].item())
+    allign = torch.full((8,), -100, dtype=torch.int64, device=DEV)
+    out = vce.fused_fwd_bwd(logits.to(torch.bfloat16), allign)
+    torch.cuda.synchronize()
+    assert math.isnan(out["loss"].item()) and int(out["n_valid"].item()) == 0
+    assert torch.all(out["grad"] == 0)
+    z = torch.randn((40, 704), device=DEV) * 2
+    t = torch.randint(0, 704, (40,), device=DEV)
+    z[0, :300] = -math.inf
+    z[0, int(t[0])] = 1.0
+    z[1, :] = -math.inf
+    z[1, int(t[1])] = 1.0
+    out = vce.fused_fwd_bwd(z, t, reduction="none")
+    torch.cuda.synchronize()
+    ref = P.oracle_for(z, t, reduction="none")
+    P.assert_loss_rows(out["loss_rows"], ref, "small -inf")
+    P.assert_grad_close(out["grad"], ref["grad"], "small -inf grad")
+    buf = z.clone()
+    ip = vce.fused_fwd_bwd(buf, t, reduction="none", grad=buf)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, out["grad"]) and torch.equal(ip["loss_rows"], out["loss_rows"])
