@@ -46,7 +46,7 @@ __device__ __forceinline__ double tab_exp1(uint32_t b, const double *tab, bool &
 
 // Sum of e^z over the 8 bf16 logits of one 16-byte vector, from the table.
 // Two logits per 32-bit word: byte offset 16 (|pattern| - kExpTabLo),
-// clamped to the zero entries, plus 8 for a negative logit; all 8 table
+// clamped to the NaN entries, plus 8 for a negative logit; all 8 table
 // reads are issued together.  Returns false (and a sum to be ignored) when
 // a pattern lies outside the table: the killed target, padding, |z| < 2^-16
 // or |z| >= 512; tab_exp8_slow then takes the vector logit by logit.

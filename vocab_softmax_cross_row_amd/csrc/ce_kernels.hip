@@ -282,13 +282,14 @@ __global__ __launch_bounds__(THREADS) void k_stats(StatsArgs a) {
 // million, and a wave pays for that path whenever one of its lanes needs it.
 
 // Entry 2 off + sign holds e^z of the pattern (kExpTabLo + off) | sign << 15,
-// off < kExpTabHalf; the last two entries (off = kExpTabHalf) are zero.
+// off < kExpTabHalf; the last two entries (off = kExpTabHalf) are NaN, so
+// that a sum which took one of them shows it.
 __global__ __launch_bounds__(256) void k_exp_table(double *tab) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= kExpTabN) return;
     const uint32_t off = (uint32_t)i >> 1, sign = (uint32_t)i & 1u;
     if (off >= (uint32_t)kExpTabHalf) {
-        tab[i] = 0.0;
+        tab[i] = __builtin_nan("");
         return;
     }
     const uint32_t b = (kExpTabLo + off) | (sign << 15);
@@ -336,12 +337,12 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
     const int64_t tail0 = v0 + nv * 8;
 
     // table index of one bf16 pattern; sets *rare when it is outside the table
-    // (a zero entry is read then, and the rare path below corrects it)
+    // (a NaN entry is read then, and the rare path below replaces it)
     auto index = [&](uint32_t b, bool &rare) {
         const uint32_t off = (b & 0x7fffu) - kExpTabLo;
         const bool in = off < (uint32_t)kExpTabHalf;
         rare |= !in;
-        return in ? (int)(2 * off + (b >> 15)) : kExpTabZero;
+        return in ? (int)(2 * off + (b >> 15)) : kExpTabNaN;
     };
     // the exact term of a pattern outside the table, and whether the online
     // form is needed instead
@@ -367,15 +368,16 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
     // their table reads in flight together.  Two logits are handled at a
     // time in the 16-bit lanes of a word:
     // - table byte offset: off = |pattern| - kExpTabLo (wrapping below),
-    //   clamped to kExpTabHalf (the zero entries), times 16, plus 8 for a
-    //   negative logit;
-    // - max: the pattern as a signed 16-bit key, ordered as the values are
-    //   (the magnitude bits of a negative pattern flipped);
+    //   clamped to kExpTabHalf (the NaN entries), times 16, plus 8 for a
+    //   negative logit; a pattern outside the table thus makes the vector's
+    //   sum NaN, which the caller tests once per vector;
+    // - max: the largest pattern as a signed 16-bit number is the largest
+    //   logit when one is positive; when all are negative it is the one
+    //   with the smallest pattern as an unsigned number, so both are kept;
     // - the sum of the logits: a bf16 dot product with (1, 1) into fp32.
-    // It returns whether the vector must be redone element by element: an
-    // offset out of range, or the target inside.
-    auto vec_common = [&](const Ch &v, int64_t vi, double &sv, s16x2 &kmax, float &zsum) {
-        u16x2 omax = {0, 0};
+    // It returns whether the target lies inside the vector.
+    auto vec_common = [&](const Ch &v, int64_t vi, double &sv, s16x2 &smax, u16x2 &umin,
+                          float &zsum) {
         double t[8];
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
         float zs = 0.0f;
@@ -383,22 +385,26 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
         for (int q = 0; q < 4; ++q) {
             const uint32_t w = v.v[q];
             const u16x2 off = __builtin_bit_cast(u16x2, w & 0x7fff7fffu) - (u16x2)(uint16_t)kExpTabLo;
-            omax = __builtin_elementwise_max(omax, off);
             const u16x2 c = __builtin_elementwise_min(off, (u16x2)(uint16_t)kExpTabHalf);
-            const uint32_t a2 = __builtin_bit_cast(uint32_t, c << (uint16_t)4) | ((w >> 12) & 0x00080008u);
+            uint32_t a2 = __builtin_bit_cast(uint32_t, c << (uint16_t)4) | ((w >> 12) & 0x00080008u);
+            // one and-or per word: without this fence the compiler forms the
+            // low offset in a separate operation
+            asm("" : "+v"(a2));
             t[2 * q] = *reinterpret_cast<const double *>(tabc + (a2 & 0xffffu));
             t[2 * q + 1] = *reinterpret_cast<const double *>(tabc + (a2 >> 16));
-            const s16x2 k = __builtin_bit_cast(s16x2, w);
-            kmax = __builtin_elementwise_max(kmax, k ^ ((k >> (int16_t)15) & (s16x2)(int16_t)0x7fff));
+            smax = __builtin_elementwise_max(smax, __builtin_bit_cast(s16x2, w));
+            umin = __builtin_elementwise_min(umin, __builtin_bit_cast(u16x2, w));
             zs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, zs, false);
         }
         zsum = zs;
         sv = ((t[0] + t[1]) + (t[2] + t[3])) + ((t[4] + t[5]) + (t[6] + t[7]));
-        return vi == tvec || omax.x >= (uint16_t)kExpTabHalf || omax.y >= (uint16_t)kExpTabHalf;
+        return vi == tvec;
     };
-    // the float value of a max key
-    auto key_value = [](int16_t k) {
-        const uint32_t b = (uint16_t)(k < 0 ? k ^ 0x7fff : k);
+    // the largest logit of vectors whose patterns all lie in the table
+    auto max_value = [](s16x2 smax, u16x2 umin) {
+        const int16_t sm = smax.x > smax.y ? smax.x : smax.y;
+        const uint16_t um = umin.x < umin.y ? umin.x : umin.y;
+        const uint32_t b = sm >= 0 ? (uint32_t)sm : (uint32_t)um;
         return __uint_as_float(b << 16);
     };
     // the element-by-element form of a vector (the target left out)
@@ -429,14 +435,16 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
     auto work_group = [&](Ch *v, int64_t base) {
         double sv[UNROLL];
         float zs[UNROLL];
-        s16x2 km = {(int16_t)-32768, (int16_t)-32768};
+        s16x2 smax = {(int16_t)-32768, (int16_t)-32768};
+        u16x2 umin = {(uint16_t)0xffff, (uint16_t)0xffff};
         bool rare[UNROLL], any = false;
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            rare[u] = vec_common(v[u], base + (int64_t)u * THREADS + tid, sv[u], km, zs[u]);
+            rare[u] = vec_common(v[u], base + (int64_t)u * THREADS + tid, sv[u], smax, umin, zs[u]);
+            rare[u] |= sv[u] != sv[u];
             any |= rare[u];
         }
-        float vm = key_value(km.x > km.y ? km.x : km.y);
+        float vm = max_value(smax, umin);
         if (__builtin_expect(any, 0)) {
             // the group's max again, from the vectors' own element maxima
             vm = ninf();
@@ -472,12 +480,13 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
         v.load(zrow + (v0 + vi * 8) * 2);
         double sv;
         float zs;
-        s16x2 km = {(int16_t)-32768, (int16_t)-32768};
+        s16x2 smax = {(int16_t)-32768, (int16_t)-32768};
+        u16x2 umin = {(uint16_t)0xffff, (uint16_t)0xffff};
         float vm;
-        if (vec_common(v, vi, sv, km, zs))
+        if (vec_common(v, vi, sv, smax, umin, zs) || sv != sv)
             vec_redo(v, vi, sv, vm);
         else
-            vm = key_value(km.x > km.y ? km.x : km.y);
+            vm = max_value(smax, umin);
         s += sv;
         sz += (double)zs;
         mx = fmaxf(mx, vm);

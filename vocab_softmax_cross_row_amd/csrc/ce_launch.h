@@ -93,10 +93,10 @@ struct StatsArgs {
 // Table of e^z for the bf16 patterns with 2^-16 <= |z| < 2^9, used by the
 // smoothed statistics of bf16 rows.  Entry 2 off + sign holds the pattern
 // (kExpTabLo + off) | sign << 15, off < kExpTabHalf; the two entries after
-// them (off = kExpTabHalf) are zero.
+// them (off = kExpTabHalf) are NaN: a read clamped to them marks its sum.
 constexpr uint32_t kExpTabLo = 0x3780; // bf16 bits of 2^-16
 constexpr int kExpTabHalf = 3200;      // magnitudes up to 2^9
-constexpr int kExpTabZero = 2 * kExpTabHalf;
+constexpr int kExpTabNaN = 2 * kExpTabHalf;
 constexpr int kExpTabN = 2 * kExpTabHalf + 2;
 
 struct MergeArgs {
