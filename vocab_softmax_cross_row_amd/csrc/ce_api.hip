@@ -193,7 +193,7 @@ int check_linear(const ce_linear_problem *p) {
     if (p->accum != CE_ACC_FP32 && p->accum != CE_ACC_KAHAN) return CE_ERR_ARG;
     if (!std::isfinite(p->filter_eps) || p->filter_eps < 0.0f) return CE_ERR_ARG;
     if (p->N < 0 || p->D < 8 || p->D % 8 != 0 || p->V < 1) return CE_ERR_SHAPE;
-    // fragment-major operands: 8 row blocks of 32 rows x (padded K) bf16 must
+    // fragment-major operands: 16 row blocks of 16 rows x (padded K) bf16 must
     // stay below 2^31 bytes (32-bit buffer offsets); counts are int32
     const int64_t kmax = ((int64_t)1 << 31) / 512 - 256;
     if (round_up(p->N, 256) > kmax || round_up(p->V, 256) > kmax ||
@@ -716,7 +716,7 @@ int ce_linear_fwd_bwd(const ce_linear_problem *prob, const void *E, const void *
         const int64_t w = std::min(l.Vc, V - c0), wp = round_up(w, 256);
         GemmArgs gg{};
         gg.A = Ef;
-        gg.B = reinterpret_cast<const char *>(Cf) + (c0 / 32) * (l.Dp / 16) * 1024;
+        gg.B = reinterpret_cast<const char *>(Cf) + (c0 / 16) * (l.Dp / 32) * 1024;
         gg.a_ks = gg.b_ks = l.Dp;
         gg.K = l.Dp;
         gg.M = N;

@@ -170,7 +170,7 @@ struct LinTileStats {
 struct GemmArgs {
     const void *A, *B;
     int64_t a_ks, b_ks; // stored (padded) K of A and B: the row pitch of the blocks
-    int a_kb0, b_kb0;   // first 16-column K block this product reads
+    int a_kb0, b_kb0;   // first 32-column K block this product reads
     int64_t K;          // K of the product (multiple of 64)
     int64_t M, N;       // valid output rows and columns
     int tiles_m, tiles_n;

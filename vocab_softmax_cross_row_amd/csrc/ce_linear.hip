@@ -3,20 +3,19 @@
 // #14, linear_cross_entropy(embeddings, classifier, labels)).
 //
 // Every product here is out[M, N] = A[M, K] B[N, K]^T with bf16 operands and
-// fp32 accumulation on v_mfma_f32_32x32x16_bf16.  Operands are kept in a
-// "fragment-major" layout: the matrix is cut into blocks of 32 rows x 16
-// K-columns (1 KB), block (rb, kb) at byte (rb * Ks/16 + kb) * 1024 where Ks
+// fp32 accumulation on v_mfma_f32_16x16x32_bf16.  Operands are kept in a
+// "fragment-major" layout: the matrix is cut into blocks of 16 rows x 32
+// K-columns (1 KB), block (rb, kb) at byte (rb * Ks/32 + kb) * 1024 where Ks
 // is the stored (padded) K, and inside a block lane L's 16 bytes at L * 16
-// hold row rb*32 + L%32, K-columns kb*16 + 8*(L/32) .. +7 -- exactly the
+// hold row rb*16 + L%16, K-columns kb*32 + 8*(L/16) .. +7 -- exactly the
 // A or B register fragment of that MFMA.  One 16-byte load per lane moves a
 // block as 1 KB of contiguous memory, straight into operand registers (A) or
 // into LDS unchanged (B), where one conflict-free ds_read_b128 reads it back
 // as a fragment.  Padding (rows to a multiple of 256, K to a multiple of 64)
 // is zero, so loads need no bounds checks.
 //
-// Accumulator layout of v_mfma_f32_32x32x16_bf16 (32 x 32 fp32, 16 values
-// per lane): register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
-// column l%32.
+// Accumulator layout of v_mfma_f32_16x16x32_bf16 (16 x 16 fp32, 4 values
+// per lane): register r of lane l holds row 4*(l/16) + r, column l%16.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -29,13 +28,13 @@
 namespace vce {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGT = 256;                 // 4 waves, each 64 rows x 256 columns of the tile
 constexpr int kTile = 256;               // output tile 256 x 256
 constexpr int kBK = 64;                  // K per LDS stage
 constexpr int kStage = 8 * 4 * 1024;     // one B stage in LDS: 8 row blocks x 4 K blocks
-constexpr int kSuperM = 4, kSuperN = 8;  // 32 tiles one XCD works on together
+constexpr int kSuperM = 8, kSuperN = 4;  // 32 tiles one XCD works on together
 
 struct LinRow {
     GradConst c;
@@ -43,10 +42,11 @@ struct LinRow {
     int32_t valid; // 1 if the row has a gradient
 };
 static_assert(sizeof(LinRow) == kLinRowBytes, "row constant size");
-static_assert(kGemmLdsBytes >= 2 * kStage + kTile * (int)sizeof(LinRow), "LDS budget");
+constexpr int kStages = 4;             // B stage buffers in LDS
+static_assert(kGemmLdsBytes >= kStages * kStage + kTile * (int)sizeof(LinRow), "LDS budget");
 
 __device__ __forceinline__ int64_t frag_off(int64_t rb, int64_t kb, int64_t Ks) {
-    return (rb * (Ks / 16) + kb) * 1024;
+    return (rb * (Ks / 32) + kb) * 1024;
 }
 
 // ---------------------------------------------------------------------------
@@ -61,9 +61,9 @@ __global__ __launch_bounds__(kRelayoutThreads) void k_relayout(RelayoutArgs a) {
     if (s >= a.Rp * a.Kp / 8) return;
     const int64_t blk = s / 64;
     const int L = (int)(s % 64);
-    const int64_t rb = blk / (a.Kp / 16), kb = blk % (a.Kp / 16);
-    const int64_t r = rb * 32 + (L & 31);
-    const int64_t k = kb * 16 + 8 * (L >> 5);
+    const int64_t rb = blk / (a.Kp / 32), kb = blk % (a.Kp / 32);
+    const int64_t r = rb * 16 + (L & 15);
+    const int64_t k = kb * 32 + 8 * (L >> 4);
     u32x4 v = {0u, 0u, 0u, 0u};
     if (r < a.R && k < a.K) v = *reinterpret_cast<const u32x4 *>(a.X + r * a.ld + k);
     *reinterpret_cast<u32x4 *>(a.Y + s * 8) = v;
@@ -91,9 +91,9 @@ __global__ __launch_bounds__(kRelayoutThreads) void k_relayout_t(RelayoutArgs a,
         u32x4 v = {0u, 0u, 0u, 0u};
         if (r < a.R && c < a.K) v = *reinterpret_cast<const u32x4 *>(a.X + r * a.ld + c);
         if (Yn && c < Kn) {
-            // lane (r % 32) + 32 ((c / 8) % 2) of block (r / 32, c / 16)
-            const int L = (int)(r & 31) + 32 * (int)((c >> 3) & 1);
-            *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(Yn) + frag_off(r >> 5, c >> 4, Kn) +
+            // lane (r % 16) + 16 ((c / 8) % 4) of block (r / 16, c / 32)
+            const int L = (int)(r & 15) + 16 * (int)((c >> 3) & 3);
+            *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(Yn) + frag_off(r >> 4, c >> 5, Kn) +
                                        L * 16) = v;
         }
 #pragma unroll
@@ -103,19 +103,19 @@ __global__ __launch_bounds__(kRelayoutThreads) void k_relayout_t(RelayoutArgs a,
         }
     }
     __syncthreads();
-    // 2 row blocks x 4 K blocks of Y = 512 slots, 2 per thread
+    // 4 row blocks x 2 K blocks of Y = 512 slots, 2 per thread
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int slot = tid + q * kRelayoutThreads;
         const int b = slot / 64, L = slot % 64;
-        const int brow = b / 4, bk = b % 4;
-        const int yr = brow * 32 + (L & 31);   // Y row in the tile  (X column)
-        const int yk = bk * 16 + 8 * (L >> 5); // Y K in the tile    (X row)
+        const int brow = b / 2, bk = b % 2;
+        const int yr = brow * 16 + (L & 15);   // Y row in the tile  (X column)
+        const int yk = bk * 32 + 8 * (L >> 4); // Y K in the tile    (X row)
         u32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             v[e] = (uint32_t)t[yk + 2 * e][yr] | ((uint32_t)t[yk + 2 * e + 1][yr] << 16);
-        const int64_t off = frag_off((y0 >> 5) + brow, (x0 >> 4) + bk, a.Kp);
+        const int64_t off = frag_off((y0 >> 4) + brow, (x0 >> 5) + bk, a.Kp);
         *reinterpret_cast<u32x4 *>(reinterpret_cast<char *>(a.Y) + off + L * 16) = v;
     }
 }
@@ -162,8 +162,11 @@ __device__ __forceinline__ float row16_sum(float x) {
 }
 
 // Tile of workgroup b.  Workgroups go round-robin over the 8 XCDs; the 32
-// consecutive workgroups of one XCD get one 4 x 8 super-tile, so they share
-// its A and B blocks in that XCD's L2.  False for the padding workgroups.
+// consecutive workgroups of one XCD get one 8 x 4 super-tile (8 row tiles,
+// 4 column tiles), so they share its A and B blocks in that XCD's L2.  Each
+// B block then serves 8 tiles: B is the large operand of the forward and G
+// products (the classifier, beyond the last-level cache), so this halves its
+// HBM reads against 4 x 8.  False for the padding workgroups.
 __device__ __forceinline__ bool tile_of(int64_t b, int tiles_m, int tiles_n, int &tm, int &tn) {
     const int64_t x = b % kXcds, j = b / kXcds;
     const int64_t s = (j / (kSuperM * kSuperN)) * kXcds + x;
@@ -196,8 +199,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t row0 = (int64_t)tm * kTile, col0 = (int64_t)tn * kTile;
 
-    // the 8 row blocks of A and of B this tile reads, as buffer resources
-    const int64_t a_span = (int64_t)8 * 32 * g.a_ks * 2, b_span = (int64_t)8 * 32 * g.b_ks * 2;
+    // the 256 rows (16 row blocks) of A and of B this tile reads, as buffer resources
+    const int64_t a_span = (int64_t)kTile * g.a_ks * 2, b_span = (int64_t)kTile * g.b_ks * 2;
     const char *abase = reinterpret_cast<const char *>(g.A) + (int64_t)tm * a_span;
     const char *bbase = reinterpret_cast<const char *>(g.B) + (int64_t)tn * b_span;
     const __amdgpu_buffer_rsrc_t ra =
@@ -205,17 +208,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
     const __amdgpu_buffer_rsrc_t rb =
         __builtin_amdgcn_make_buffer_rsrc((void *)bbase, 0, (int)b_span, 0x00020000);
     int nk = (int)(g.K / kBK);
-    const int a_kbs = (int)(g.a_ks / 16), b_kbs = (int)(g.b_ks / 16);
+    const int a_kbs = (int)(g.a_ks / 32), b_kbs = (int)(g.b_ks / 32);
     // the filtered K walk belongs to the backward products only; the G
     // product with FILT records keep flags and walks all of K
     constexpr bool kWalk = FILT && (EPI == GEMM_STORE || EPI == GEMM_ADD || EPI == GEMM_KAHAN);
 
     // Filtered K walk: the kept 256-wide K tiles of this output row tile are
-    // copied into LDS after the two stage buffers (free during the main
-    // loop), and stage kt reads stored stage kstage(kt) = 4 list[kt/4] + kt%4.
+    // copied into LDS after the stage buffers (free during the main loop),
+    // and stage kt reads stored stage kstage(kt) = 4 list[kt/4] + kt%4.
     // km1 / km2 hold kstage(kt + 1) and kstage(kt + 2) while stage kt runs;
     // each list entry is read from LDS one stage before it is needed.
-    uint16_t *klds = reinterpret_cast<uint16_t *>(lbase + 2 * kStage);
+    uint16_t *klds = reinterpret_cast<uint16_t *>(lbase + kStages * kStage);
     if constexpr (kWalk) {
         nk = 4 * g.kcnt[tm];
         const uint16_t *src = g.klist + (int64_t)tm * g.klist_pitch;
@@ -237,53 +240,69 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
         }
     };
 
-    // Wave w owns rows 64w .. 64w+63 of the tile and all 256 columns
-    // (2 x 8 accumulators of 32 x 32).  Its A fragments are its own: they go
-    // from global memory straight into the MFMA operand registers, each
-    // K block's pair reloaded with the next stage as soon as its MFMAs have
-    // issued, so a load has a whole stage to land.  B is shared by the four
-    // waves: global -> registers -> LDS (two stage buffers).  Each lane owns
-    // 8 B slots of 16 bytes per stage (row blocks 2w and 2w+1, K blocks
-    // 0..3); while stage kt is multiplied out of one buffer, K groups 0..2
-    // write the slots (stage kt+1, loaded one stage earlier) to the other
-    // buffer and at once reload them with stage kt+2.  The stage's one
-    // barrier follows group 2, so group 3 already reads the first B
-    // fragments of stage kt+1.  Within a group each MFMA is followed by one
-    // LDS read, or by one slot's write and reload, so the matrix pipe is
-    // never left behind a burst of memory instructions.  Only B passes
-    // through LDS: half the LDS traffic of a 2 x 2 wave layout, which
-    // matters because a bf16 GEMM on this chip runs at a power-limited
-    // clock, and moved bytes cost power.
-    bf16x8 fa[2][4]; // [row block][K block]
+    // Wave w owns rows 64w .. 64w+63 of the tile (16-row blocks 4w .. 4w+3)
+    // and all 256 columns: 4 x 16 accumulators of 16 x 16.  A stage is
+    // 64 K deep, two K steps of 32; it is walked as 32 positions (K step
+    // p / 16, column block p % 16), each 4 MFMAs, one per row block.
+    // - A fragments are the wave's own: global memory straight into operand
+    //   registers, each K step's four reloaded with the next stage right
+    //   after the step's last MFMAs, so a load has half a stage to land.
+    // - B is shared by the four waves: global -> LDS directly (buffer loads
+    //   with the LDS as destination, no registers), four stage buffers
+    //   (stage kt in buffer kt % 4).  Each lane owns 8 slots of 16 bytes per
+    //   stage (row blocks 4w .. 4w+3, both K blocks); positions 0..7 of
+    //   stage kt load the slots of stage kt+2, so a load has a stage and a
+    //   half to land.
+    // - B fragments are read from LDS kAhead positions before their MFMAs,
+    //   one read per position, across the stage boundary too: a rolling
+    //   window of kAhead + 1 fragments instead of two full sets.
+    // - One barrier per stage, at position 32 - kAhead, just before the
+    //   first read of stage kt+1's buffer: it first waits for this wave's
+    //   slot loads of stage kt+1 (issued in stage kt-1; vector memory loads
+    //   complete in order, so the loads issued after them may stay in
+    //   flight), so the read sees every wave's slots.  A buffer is loaded
+    //   again (stage kt+4, in stage kt+2) only after every wave has used its
+    //   fragments in MFMAs and passed stage kt+1's barrier, so no load can
+    //   overtake a read.
+    // - Each MFMA is followed by at most one memory instruction
+    //   (sched_group_barrier), so the matrix pipe never waits behind a
+    //   burst of them.
+    // Only B passes through LDS: half the LDS traffic of a 2 x 2 wave
+    // layout.  Moving B is the dearest part of the loop: without its loads
+    // and LDS writes the product would take 20% less time (measured), and
+    // the direct-to-LDS form is cheaper than staging through registers.  A bf16 GEMM on this chip runs at a power-limited clock, and
+    // the 16 x 16 x 32 instruction costs less energy per flop than the
+    // 32 x 32 x 16 one (with random operands, MFMAs alone sustain 1.99
+    // against 1.75 PFLOP/s, at 1.92 against 1.67 GHz).
+    constexpr int kAhead = 8;
+    bf16x8 fa[4][2]; // [row block][K step]
     // ks: stored stage index (kstage of the loop's stage)
-    auto load_a = [&](int ks, int r, int kb) {
-        fa[r][kb] = __builtin_bit_cast(
+    auto load_a = [&](int ks, int i, int st) {
+        fa[i][st] = __builtin_bit_cast(
             bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-                        ra, lane * 16, ((2 * wave + r) * a_kbs + g.a_kb0 + ks * 4 + kb) * 1024, 0));
+                        ra, lane * 16, ((4 * wave + i) * a_kbs + g.a_kb0 + ks * 2 + st) * 1024, 0));
     };
-    u32x4 stg[8];
-    auto load_b = [&](int ks, int q) {
-        stg[q] = __builtin_amdgcn_raw_buffer_load_b128(
-            rb, lane * 16, ((2 * wave + (q >> 2)) * b_kbs + g.b_kb0 + ks * 4 + (q & 3)) * 1024, 0);
+    // slot q of stage ks into buffer buf: each lane's 16 bytes land at its
+    // own place in the 1 KB block (the wave-uniform block address goes to M0)
+    typedef __attribute__((address_space(3))) void lds_void_t;
+    auto load_b = [&](int ks, int buf, int q) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rb, (lds_void_t *)(lbase + buf * kStage + ((4 * wave + (q >> 1)) * 2 + (q & 1)) * 1024), 16,
+            lane * 16, ((4 * wave + (q >> 1)) * b_kbs + g.b_kb0 + ks * 2 + (q & 1)) * 1024, 0, 0);
     };
-    auto write_b = [&](int buf, int q) {
-        *reinterpret_cast<u32x4 *>(lbase + buf * kStage + ((2 * wave + (q >> 2)) * 4 + (q & 3)) * 1024 +
-                                   lane * 16) = stg[q];
+    // the B fragment of position p of a stage buffer
+    auto read_b = [&](int buf, int p) {
+        return *reinterpret_cast<const bf16x8 *>(lbase + buf * kStage + ((p & 15) * 2 + (p >> 4)) * 1024 +
+                                                 lane * 16);
     };
-    bf16x8 fb[2][8];
-    auto read_b = [&](int buf, int kb, int set) {
-        const char *st = lbase + buf * kStage;
+    f32x4 acc[4][16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            fb[set][j] = *reinterpret_cast<const bf16x8 *>(st + (j * 4 + kb) * 1024 + lane * 16);
-    };
-    f32x16 acc[2][8];
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 16; ++j)
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+            for (int r = 0; r < 4; ++r) acc[i][j][r] = 0.0f;
+    bf16x8 carry[kAhead]; // B fragments of the next stage's first positions
     int km1 = 1, km2 = 2;
     if (nk > 0) {
     const int k0 = kstage(0);
@@ -292,79 +311,73 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
         km2 = kstage(2);
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) load_b(k0, q);
+    for (int q = 0; q < 8; ++q) load_b(k0, 0, q);
 #pragma unroll
-    for (int r = 0; r < 2; ++r)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) load_a(k0, r, kb);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) write_b(0, q);
+        for (int st = 0; st < 2; ++st) load_a(k0, i, st);
     if (nk > 1) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) load_b(km1, q);
+        for (int q = 0; q < 8; ++q) load_b(km1, 1, q);
     }
-
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    read_b(0, 0, 0);
+#pragma unroll
+    for (int x = 0; x < kAhead; ++x) carry[x] = read_b(0, x);
 
-    constexpr int q_lo[4] = {0, 3, 6, 8}; // B slots written in K groups 0, 1, 2
-    // MORE1: stage kt+1 exists (write its B, load its A, read its first B
-    // fragments in group 3); MORE2: stage kt+2 exists (load its B).  The
-    // flags are compile-time so the loop body has no branches and every
-    // wait before a use stays a constant count of later loads.
+    // MORE1: stage kt+1 exists (load its A, read its first B fragments);
+    // MORE2: stage kt+2 exists (load its B).  The flags are
+    // compile-time so the loop body has no branches and every wait before a
+    // use stays a constant count of later loads.
     auto run_stage = [&](int kt, auto MORE1, auto MORE2) {
         constexpr bool more1 = decltype(MORE1)::value, more2 = decltype(MORE2)::value;
-        const int cb = kt & 1, nb = cb ^ 1;
+        const int cb = kt % kStages, nb = (kt + 1) % kStages;
         // stored stage indices of stages kt + 1 and kt + 2
         const int s1 = kWalk ? km1 : kt + 1, s2 = kWalk ? km2 : kt + 2;
+        bf16x8 f[32 + kAhead];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int cur = kb & 1;
+        for (int x = 0; x < kAhead; ++x) f[x] = carry[x];
+#pragma unroll
+        for (int p = 0; p < 32; ++p) {
             __builtin_amdgcn_sched_barrier(0);
-            const bool rd = kb < 3 || more1;
-            if (kb < 3) read_b(cb, kb + 1, cur ^ 1);
-            else if (more1) read_b(nb, 0, cur ^ 1);
-            const int nq = kb < 3 ? q_lo[kb + 1] - q_lo[kb] : 0;
-            if (kb < 3) {
-#pragma unroll
-                for (int q = q_lo[kb]; q < q_lo[kb + 1]; ++q) {
-                    if constexpr (more1) write_b(nb, q);
-                    if constexpr (more2) load_b(s2, q);
-                }
+            if (p == 32 - kAhead && more1) {
+                // issued after this wave's slot loads of stage kt+1 (stage
+                // kt-1, positions 0..7): stage kt-1's 8 A loads, this
+                // stage's 8 slot loads when stage kt+2 exists, and this
+                // stage's 4 A loads of position 15
+                static_assert(32 - kAhead > 15, "the barrier follows position 15's A loads");
+                if constexpr (more2) asm volatile("s_waitcnt vmcnt(20)\n\ts_barrier" ::: "memory");
+                else asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
             }
+            const int pr = p + kAhead;
+            const bool rd = pr < 32 || more1;
+            if (pr < 32) f[pr] = read_b(cb, pr);
+            else if (more1) f[pr] = read_b(nb, pr - 32);
+            const bool ld = p < 8 && more2;
+            if (ld) load_b(s2, (kt + 2) % kStages, p);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 4; ++i)
+                acc[i][p & 15] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i][p >> 4], f[p],
+                                                                         acc[i][p & 15], 0, 0, 0);
+            const bool lda = (p & 15) == 15 && more1;
+            if (lda) {
 #pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i][kb], fb[cur][j],
-                                                                         acc[i][j], 0, 0, 0);
-            if constexpr (more1) {
-                load_a(s1, 0, kb);
-                load_a(s1, 1, kb);
+                for (int i = 0; i < 4; ++i) load_a(s1, i, p >> 4);
             }
-            // issue order: MFMA, LDS read (x8); MFMA, LDS write, B load;
-            // MFMA, the two A loads
-            if (rd) {
-#pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // one MFMA
-                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); // one LDS read
-                }
-            }
-#pragma unroll
-            for (int w = 0; w < 3; ++w) {
-                if (w < nq) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if (more1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0); // LDS write
-                    if (more2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); // global load
-                }
-            }
-            if (more1) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
-            }
+            // issue order: MFMA, LDS read; MFMA; MFMA, B load; MFMA, the
+            // four A loads
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (rd) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (ld) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (lda) __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);
             __builtin_amdgcn_sched_barrier(0);
-            if (kb == 2) __syncthreads();
+        }
+        if constexpr (more1) {
+#pragma unroll
+            for (int x = 0; x < kAhead; ++x) carry[x] = f[32 + x];
         }
         if constexpr (kWalk) {
             // the next stage's pair (stage kt + 3 read from the list now)
@@ -390,11 +403,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
     // a write issued that soon after the MFMA producing its source read a
     // stale value (the hazard padding inserted for it was too short).
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) asm volatile("" : "+a"(acc[i][j]));
+        for (int j = 0; j < 16; ++j) asm volatile("" : "+a"(acc[i][j]));
     // and 32 wait states on top of the compiler's own padding, whatever the
-    // order of the last K group's MFMAs (once per tile)
+    // order of the last position's MFMAs (once per tile)
 #pragma unroll
     for (int q = 0; q < 4; ++q) asm volatile("s_nop 7");
     __builtin_amdgcn_sched_barrier(0);
@@ -405,17 +418,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
     // through the wave's own LDS slab so that the row-wise work and the
     // global accesses are contiguous: lanes 16q..16q+15 then own row
     // 4*it + q of the block and 8 consecutive columns each.
-    const int h = lane >> 5, lc = lane & 31;
     constexpr int kPitch = 132; // floats per slab row (keeps 16-byte reads spread over banks)
     float *slab = reinterpret_cast<float *>(lbase) + wave * 32 * kPitch;
     const int sub = lane >> 4, c8 = (lane & 15) * 8; // row-pass lane role
+    // accumulator (i, j) register r of lane l: tile row 16 i + 4 (l / 16) + r
+    // of the wave's rows, column 16 j + l % 16
     auto stage = [&](int e) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                slab[(8 * (r >> 2) + 4 * h + (r & 3)) * kPitch + j * 32 + lc] =
-                    acc[e >> 1][4 * (e & 1) + j][r];
+            for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    slab[(16 * ii + 4 * sub + r) * kPitch + jj * 16 + (lane & 15)] =
+                        acc[2 * (e >> 1) + ii][8 * (e & 1) + jj][r];
     };
     auto blk_row = [&](int e) { return wave * 64 + (e >> 1) * 32; }; // first tile row of block e
     auto blk_col = [&](int e) { return (e & 1) * 128; };            // first tile column
@@ -580,8 +596,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
 #pragma unroll
                 for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(gv[2 * e], gv[2 * e + 1]);
                 *reinterpret_cast<u32x4 *>(bslab + rl * kBPitch + c8) = w;
-                const int64_t off = frag_off(n >> 5, v0 >> 4, g.ldg) +
-                                    (int64_t)((n & 31) + 32 * ((v0 & 15) >> 3)) * 16;
+                const int64_t off = frag_off(n >> 4, v0 >> 5, g.ldg) +
+                                    (int64_t)((n & 15) + 16 * ((v0 & 31) >> 3)) * 16;
                 *reinterpret_cast<u32x4 *>(G + off) = w;
             }
             __syncthreads();
@@ -597,8 +613,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
                            ((uint32_t)bslab[(8 * tau + 2 * e + 1) * kBPitch + c] << 16);
                 const int64_t v = col0 + blk_col(e) + c;
                 const int64_t n0 = row0 + blk_row(e) + 8 * tau;
-                const int64_t off = frag_off(v >> 5, n0 >> 4, g.ldgt) +
-                                    (int64_t)((v & 31) + 32 * ((n0 & 15) >> 3)) * 16;
+                const int64_t off = frag_off(v >> 4, n0 >> 5, g.ldgt) +
+                                    (int64_t)((v & 15) + 16 * ((n0 & 31) >> 3)) * 16;
                 *reinterpret_cast<u32x4 *>(GT + off) = w;
             }
         }
