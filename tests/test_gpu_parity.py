@@ -632,6 +632,41 @@ def test_smoothed_bf16_statistics_edge_values(shard):
     P.assert_grad_close(g, ref["grad"], "table edges grad")
 
 
+def test_smoothed_bf16_statistics_max_by_sign():
+    """The smoothed bf16 statistics take the running max of the patterns
+    read as another 16-bit float format; the max must come out right
+    whatever the signs: rows all negative, all positive, negative but for
+    one small positive logit, and negative but for a large positive target
+    (which the non-target max leaves out).  40000 columns: four whole
+    groups of vectors per row, then the per-vector tail."""
+    c, logits, target = _case(S.PAGE, 64, 40000, 149, eps=0.1)
+    g = torch.Generator().manual_seed(149)
+    z = logits.float().cpu()
+    t = target.cpu()
+    a = z.abs()
+    z[0:16] = -a[0:16] - 1.0
+    z[16:32] = a[16:32] + 1.0
+    z[32:48] = -a[32:48] - 2.0
+    cols = torch.randint(0, 40000, (16,), generator=g)
+    for i in range(16):
+        r = 32 + i
+        col = int(cols[i]) if int(cols[i]) != int(t[r]) else (int(cols[i]) + 1) % 40000
+        z[r, col] = 0.0078125 * (i + 1)
+    z[48:64] = -a[48:64] - 3.0
+    for r in range(48, 64):
+        if 0 <= int(t[r]) < 40000:
+            z[r, int(t[r])] = 50.0
+    logits = z.to(torch.bfloat16).to(DEV)
+    eps = 0.1
+    f = vce.forward(logits, target, label_smoothing=eps)
+    torch.cuda.synchronize()
+    zz = to_numpy_logits(logits)
+    _stats_check(f["stats"], O.shard_stats(zz, t.numpy(), 0), t.numpy(), 40000,
+                 "max by sign", eps)
+    ref = P.oracle_for(logits, target, eps=eps)
+    P.assert_loss_rows(f["loss_rows"], ref, "max by sign")
+
+
 @pytest.mark.parametrize("V", [6144, 24576])
 @pytest.mark.parametrize("eps", [0.1, 0.6])
 def test_smoothed_gradient_where_p_meets_eps_over_v(eps, V):

@@ -297,8 +297,8 @@ __global__ __launch_bounds__(256) void k_exp_table(double *tab) {
 }
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
-typedef int16_t s16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // One (row, column chunk) unit of the smoothed bf16 statistics, with the
 // table already in LDS.
@@ -371,13 +371,16 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
     //   clamped to kExpTabHalf (the NaN entries), times 16, plus 8 for a
     //   negative logit; a pattern outside the table thus makes the vector's
     //   sum NaN, which the caller tests once per vector;
-    // - max: the largest pattern as a signed 16-bit number is the largest
-    //   logit when one is positive; when all are negative it is the one
-    //   with the smallest pattern as an unsigned number, so both are kept;
+    // - max: a running max of the patterns read as fp16 numbers.  Like
+    //   bf16, fp16 orders sign-magnitude patterns as their values, so the
+    //   largest fp16 reading is the largest logit, for every pattern in the
+    //   table (bf16 2^-16 .. 2^9 reads as a normal fp16: exponent field 13
+    //   to 16); the NaN-propagating maximum takes two words per operation
+    //   and needs no canonicalizing, and a pattern outside the table sends
+    //   the group to the element-by-element form anyway;
     // - the sum of the logits: a bf16 dot product with (1, 1) into fp32.
     // It returns whether the target lies inside the vector.
-    auto vec_common = [&](const Ch &v, int64_t vi, double &sv, s16x2 &smax, u16x2 &umin,
-                          float &zsum) {
+    auto vec_common = [&](const Ch &v, int64_t vi, double &sv, f16x2 &hmax, float &zsum) {
         double t[8];
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
         float zs = 0.0f;
@@ -392,8 +395,7 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
             asm("" : "+v"(a2));
             t[2 * q] = *reinterpret_cast<const double *>(tabc + (a2 & 0xffffu));
             t[2 * q + 1] = *reinterpret_cast<const double *>(tabc + (a2 >> 16));
-            smax = __builtin_elementwise_max(smax, __builtin_bit_cast(s16x2, w));
-            umin = __builtin_elementwise_min(umin, __builtin_bit_cast(u16x2, w));
+            hmax = __builtin_elementwise_maximum(hmax, __builtin_bit_cast(f16x2, w));
             zs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), ones, zs, false);
         }
         zsum = zs;
@@ -401,12 +403,12 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
         return vi == tvec;
     };
     // the largest logit of vectors whose patterns all lie in the table
-    auto max_value = [](s16x2 smax, u16x2 umin) {
-        const int16_t sm = smax.x > smax.y ? smax.x : smax.y;
-        const uint16_t um = umin.x < umin.y ? umin.x : umin.y;
-        const uint32_t b = sm >= 0 ? (uint32_t)sm : (uint32_t)um;
-        return __uint_as_float(b << 16);
+    auto max_value = [](f16x2 hmax) {
+        const _Float16 m = hmax.x > hmax.y ? hmax.x : hmax.y;
+        return __uint_as_float((uint32_t)__builtin_bit_cast(uint16_t, m) << 16);
     };
+    const f16x2 hmax0 = {__builtin_bit_cast(_Float16, (uint16_t)0xfc00u),
+                         __builtin_bit_cast(_Float16, (uint16_t)0xfc00u)}; // fp16 -inf
     // the element-by-element form of a vector (the target left out)
     auto vec_redo = [&](const Ch &v, int64_t vi, double &sv, float &vm) {
         const int64_t col = v0 + vi * 8;
@@ -435,16 +437,15 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
     auto work_group = [&](Ch *v, int64_t base) {
         double sv[UNROLL];
         float zs[UNROLL];
-        s16x2 smax = {(int16_t)-32768, (int16_t)-32768};
-        u16x2 umin = {(uint16_t)0xffff, (uint16_t)0xffff};
+        f16x2 hmax = hmax0;
         bool rare[UNROLL], any = false;
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
-            rare[u] = vec_common(v[u], base + (int64_t)u * THREADS + tid, sv[u], smax, umin, zs[u]);
+            rare[u] = vec_common(v[u], base + (int64_t)u * THREADS + tid, sv[u], hmax, zs[u]);
             rare[u] |= sv[u] != sv[u];
             any |= rare[u];
         }
-        float vm = max_value(smax, umin);
+        float vm = max_value(hmax);
         if (__builtin_expect(any, 0)) {
             // the group's max again, from the vectors' own element maxima
             vm = ninf();
@@ -480,13 +481,12 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
         v.load(zrow + (v0 + vi * 8) * 2);
         double sv;
         float zs;
-        s16x2 smax = {(int16_t)-32768, (int16_t)-32768};
-        u16x2 umin = {(uint16_t)0xffff, (uint16_t)0xffff};
+        f16x2 hmax = hmax0;
         float vm;
-        if (vec_common(v, vi, sv, smax, umin, zs) || sv != sv)
+        if (vec_common(v, vi, sv, hmax, zs) || sv != sv)
             vec_redo(v, vi, sv, vm);
         else
-            vm = max_value(smax, umin);
+            vm = max_value(hmax);
         s += sv;
         sz += (double)zs;
         mx = fmaxf(mx, vm);
