@@ -10,6 +10,11 @@ pre-pass, the row-resident fused kernel (max, non-target sum, finalize,
 gradient) and the loss reduction.  Inputs are generated on the GPU from a
 fixed seed before timing and stay in HBM.  Prints one JSON line.
 
+Every timed section runs W untimed calls first (default 10): after the GPU
+has been idle, the first steps of an HBM-bound loop run slow while the clocks
+come back up (split-V steps right after a synchronize: 2.46, 2.37, 2.32,
+2.31, 2.29 ms, then 2.24-2.26 from about the eighth step on).
+
 Algorithmic bytes of a fused step: the logits of every non-ignored row read
 once (an ignored row's logits are not needed), every gradient row written
 once (zeros for ignored rows), and per row the int64 target read and the
@@ -229,7 +234,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--no-split", action="store_true", help="skip the split-V measurement")

@@ -222,9 +222,8 @@ int ce_fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtyp
  * in the library, one per GPU, held until the process ends; the call
  * allocates nothing.  The caller still passes inputs and outputs.
  *   - Problems whose ce_workspace_bytes(prob, CE_OP_FUSED) exceeds
- *     CE_NOALLOC_SCRATCH_BYTES (about 139,000 rows at any row length; fewer
- *     with label smoothing of bf16 rows, which adds a 51 KB table) return
- *     CE_ERR_WORKSPACE before any launch.
+ *     CE_NOALLOC_SCRATCH_BYTES (about 139,000 rows at any row length)
+ *     return CE_ERR_WORKSPACE before any launch.
  *   - The stream must belong to the current device (CE_ERR_ARG otherwise).
  *   - Every call on one GPU shares that GPU's array: calls that overlap in
  *     time on one GPU (two streams, two threads) race and give wrong

@@ -27,6 +27,9 @@ def hipcc():
 
 
 def build(verbose: bool = False) -> str:
+    # the e^z table of the smoothed bf16 statistics, compiled into the code object
+    subprocess.run([sys.executable, os.path.join(CSRC, "gen_exp_table.py"),
+                    os.path.join(CSRC, "ce_exp_table.inc")], check=True, capture_output=True)
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -131,12 +131,11 @@ struct Layout {
     size_t fin;       // [T] ce_row_final
     size_t loss_rows; // [T] float
     size_t n_valid;   // [1] int32
-    size_t exp_tab;   // e^z table of the smoothed bf16 statistics
     size_t total;
 };
 
 Layout layout(const ce_problem *p, int op) {
-    Layout l{0, 0, 0, 0, 0, 0};
+    Layout l{0, 0, 0, 0, 0};
     const int64_t T = std::max<int64_t>(p->T, 0);
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -145,18 +144,15 @@ Layout layout(const ce_problem *p, int op) {
         return o;
     };
     const Plan pl = plan_chunks(T, p->V_local);
-    const size_t tab = p->label_smoothing > 0.0f ? (size_t)kExpTabN * sizeof(double) : 0;
     if (op == CE_OP_FORWARD) {
         l.partial = take(pl.nchunks > 1 ? (size_t)pl.nchunks * T * sizeof(ce_row_stats) : 0);
         l.loss_rows = take((size_t)T * sizeof(float));
         l.n_valid = take(sizeof(int32_t));
-        l.exp_tab = take(tab);
     } else if (op == CE_OP_FUSED) {
         l.partial = take((size_t)std::max(pl.nchunks, 1) * T * sizeof(ce_row_stats));
         l.fin = take((size_t)T * sizeof(ce_row_final));
         l.loss_rows = take((size_t)T * sizeof(float));
         l.n_valid = take(sizeof(int32_t));
-        l.exp_tab = take(tab);
     } else if (op == CE_OP_MERGE) {
         l.loss_rows = take((size_t)T * sizeof(float));
         l.n_valid = take(sizeof(int32_t));
@@ -321,15 +317,13 @@ int ce_forward(const ce_problem *prob, const void *logits, int logits_dtype,
     if ((rc = check_ws(prob, CE_OP_FORWARD, ws, ws_bytes, &l)) != CE_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
-    if (whole) {
-        int32_t *nv = n_valid ? n_valid : at<int32_t>(ws, l.n_valid);
-        VCE_TRY(launch_count(target, p.T, p.ignore_index, p.V_total, nv, err_count, s));
-        if (p.T == 0) {
+    int32_t *nv = n_valid ? n_valid : at<int32_t>(ws, l.n_valid);
+    if (p.T == 0) {
+        if (whole) {
+            VCE_TRY(launch_count(target, p.T, p.ignore_index, p.V_total, nv, err_count, s));
             if (loss && p.reduction != CE_RED_NONE)
                 VCE_TRY(launch_reduce(nullptr, 0, p.reduction, nv, loss, s));
-            return CE_OK;
         }
-    } else if (p.T == 0) {
         return CE_OK;
     }
 
@@ -349,11 +343,8 @@ int ce_forward(const ce_problem *prob, const void *logits, int logits_dtype,
     sa.smoothing = p.label_smoothing > 0.0f;
     sa.exp_tab = nullptr;
     const bool vec = stream_vec_ok(logits, p.ld, logits_dtype, nullptr, 0, CE_F32);
-    if (sa.smoothing && vec && logits_dtype == CE_BF16) {
-        double *tab = at<double>(ws, l.exp_tab);
-        VCE_TRY(launch_exp_table(tab, s));
-        sa.exp_tab = tab;
-    }
+    if (sa.smoothing && vec && logits_dtype == CE_BF16)
+        VCE_TRY(exp_table_address(s, &sa.exp_tab));
     VCE_TRY(launch_stats(sa, logits_dtype, vec, s));
 
     MergeArgs ma;
@@ -375,12 +366,14 @@ int ce_forward(const ce_problem *prob, const void *logits, int logits_dtype,
     ma.fin = whole ? fin : nullptr;
     float *lr = loss_rows ? loss_rows : at<float>(ws, l.loss_rows);
     ma.loss_rows = whole ? lr : nullptr;
+    // a whole-vocabulary call also counts its targets, in the merge launch
+    ma.count = whole ? 1 : 0;
+    ma.n_valid = nv;
+    ma.err_count = err_count;
     if (ma.stats_out || ma.fin || ma.loss_rows) VCE_TRY(launch_merge(ma, s));
 
-    if (whole && loss && p.reduction != CE_RED_NONE) {
-        const int32_t *nv = n_valid ? n_valid : at<int32_t>(ws, l.n_valid);
+    if (whole && loss && p.reduction != CE_RED_NONE)
         VCE_TRY(launch_reduce(lr, p.T, p.reduction, nv, loss, s));
-    }
     return CE_OK;
 }
 
@@ -398,8 +391,8 @@ int ce_merge_shard_stats(const ce_problem *prob, int n_shards, const ce_row_stat
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     int32_t *nv = n_valid ? n_valid : at<int32_t>(ws, l.n_valid);
-    VCE_TRY(launch_count(target, p.T, p.ignore_index, p.V_total, nv, err_count, s));
     float *lr = loss_rows ? loss_rows : at<float>(ws, l.loss_rows);
+    if (p.T == 0) VCE_TRY(launch_count(target, p.T, p.ignore_index, p.V_total, nv, err_count, s));
     if (p.T > 0) {
         MergeArgs ma;
         ma.in = shard_stats;
@@ -412,6 +405,10 @@ int ce_merge_shard_stats(const ce_problem *prob, int n_shards, const ce_row_stat
         ma.stats_out = nullptr;
         ma.fin = fin;
         ma.loss_rows = lr;
+        // the target count runs as one more workgroup of the merge
+        ma.count = 1;
+        ma.n_valid = nv;
+        ma.err_count = err_count;
         VCE_TRY(launch_merge(ma, s));
     }
     if (loss && p.reduction != CE_RED_NONE)
@@ -513,10 +510,8 @@ int fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtype,
             fa.eps = p.label_smoothing;
             fa.exp_tab = nullptr;
             if (p.label_smoothing > 0.0f && fused_table(logits_dtype, p.V_local)) {
-                // the smoothed sums read e^z from a table (built per call)
-                double *tab = at<double>(ws, l.exp_tab);
-                VCE_TRY(launch_exp_table(tab, s));
-                fa.exp_tab = tab;
+                // the smoothed sums read e^z from the code object's table
+                VCE_TRY(exp_table_address(s, &fa.exp_tab));
             }
             VCE_TRY(launch_fused_resident(fa, logits_dtype, grad_dtype, p.T, vec, s));
         } else {
@@ -536,11 +531,8 @@ int fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtype,
             sa.out = at<ce_row_stats>(ws, l.partial);
             sa.smoothing = p.label_smoothing > 0.0f;
             sa.exp_tab = nullptr;
-            if (sa.smoothing && svec && logits_dtype == CE_BF16) {
-                double *tab = at<double>(ws, l.exp_tab);
-                VCE_TRY(launch_exp_table(tab, s));
-                sa.exp_tab = tab;
-            }
+            if (sa.smoothing && svec && logits_dtype == CE_BF16)
+                VCE_TRY(exp_table_address(s, &sa.exp_tab));
             VCE_TRY(launch_stats(sa, logits_dtype, svec, s));
 
             ce_row_final *fin = at<ce_row_final>(ws, l.fin);

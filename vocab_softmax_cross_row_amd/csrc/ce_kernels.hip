@@ -18,6 +18,7 @@
 #include <algorithm>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include "ce_device.h"
 #include "ce_launch.h"
@@ -33,16 +34,18 @@ namespace vce {
 constexpr int kCountThreads = 1024;
 constexpr int kPerThread = 16;
 
-__global__ __launch_bounds__(kCountThreads) void k_count(const int64_t *__restrict__ target,
-                                                         int64_t T, int64_t ignore_index,
-                                                         int64_t V_total, int32_t *n_valid,
-                                                         int32_t *err_count) {
+// The count by one workgroup of THREADS threads (k_count, and the extra
+// workgroup of k_merge).
+template <int THREADS>
+__device__ __forceinline__ void count_targets(const int64_t *__restrict__ target, int64_t T,
+                                              int64_t ignore_index, int64_t V_total,
+                                              int32_t *n_valid, int32_t *err_count) {
     int nv = 0, nb = 0;
-    for (int64_t base = 0; base < T; base += (int64_t)kCountThreads * kPerThread) {
+    for (int64_t base = 0; base < T; base += (int64_t)THREADS * kPerThread) {
         int64_t t[kPerThread];
 #pragma unroll
         for (int u = 0; u < kPerThread; ++u) {
-            const int64_t r = base + (int64_t)u * kCountThreads + threadIdx.x;
+            const int64_t r = base + (int64_t)u * THREADS + threadIdx.x;
             t[u] = (r < T) ? target[r] : ignore_index;
         }
 #pragma unroll
@@ -56,7 +59,7 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const int64_t *__restri
     }
     nv = wave_sum(nv);
     nb = wave_sum(nb);
-    __shared__ int part[2][kCountThreads / kWave];
+    __shared__ int part[2][THREADS / kWave];
     const int wv = threadIdx.x / kWave;
     if ((threadIdx.x & (kWave - 1)) == 0) {
         part[0][wv] = nv;
@@ -65,13 +68,20 @@ __global__ __launch_bounds__(kCountThreads) void k_count(const int64_t *__restri
     __syncthreads();
     if (threadIdx.x == 0) {
         int x = 0, y = 0;
-        for (int i = 0; i < kCountThreads / kWave; ++i) {
+        for (int i = 0; i < THREADS / kWave; ++i) {
             x += part[0][i];
             y += part[1][i];
         }
         if (n_valid) *n_valid = x;
         if (err_count) *err_count = y;
     }
+}
+
+__global__ __launch_bounds__(kCountThreads) void k_count(const int64_t *__restrict__ target,
+                                                         int64_t T, int64_t ignore_index,
+                                                         int64_t V_total, int32_t *n_valid,
+                                                         int32_t *err_count) {
+    count_targets<kCountThreads>(target, T, ignore_index, V_total, n_valid, err_count);
 }
 
 // ===========================================================================
@@ -282,19 +292,19 @@ __global__ __launch_bounds__(THREADS) void k_stats(StatsArgs a) {
 // million, and a wave pays for that path whenever one of its lanes needs it.
 
 // Entry 2 off + sign holds e^z of the pattern (kExpTabLo + off) | sign << 15,
-// off < kExpTabHalf; the last two entries (off = kExpTabHalf) are NaN, so
-// that a sum which took one of them shows it.
-__global__ __launch_bounds__(256) void k_exp_table(double *tab) {
-    const int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= kExpTabN) return;
-    const uint32_t off = (uint32_t)i >> 1, sign = (uint32_t)i & 1u;
-    if (off >= (uint32_t)kExpTabHalf) {
-        tab[i] = __builtin_nan("");
-        return;
-    }
-    const uint32_t b = (kExpTabLo + off) | (sign << 15);
-    tab[i] = exp((double)__uint_as_float(b << 16));
-}
+// off < kExpTabHalf, the double nearest to the exact value; the last two
+// entries (off = kExpTabHalf) are NaN, so that a sum which took one of them
+// shows it.  The values are written by gen_exp_table.py when the library is
+// built, and live in the code object: no call builds the table.  Not const:
+// a const array would have internal linkage, and since kernels read it only
+// through a pointer argument the device compiler would drop it, leaving the
+// runtime nothing to find when the host asks for its address.
+__device__ double kExpTable[kExpTabN] = {
+#include "ce_exp_table.inc"
+};
+static_assert(CE_EXP_TABLE_LO == kExpTabLo && CE_EXP_TABLE_HALF == kExpTabHalf &&
+                  CE_EXP_TABLE_ENTRIES == kExpTabN,
+              "ce_exp_table.inc was written for another table layout");
 
 typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -561,6 +571,13 @@ __global__ __launch_bounds__(THREADS) void k_stats_tab(StatsArgs a, const double
 constexpr int kMergeThreads = 256;
 
 __global__ __launch_bounds__(kMergeThreads) void k_merge(MergeArgs a) {
+    if (a.count && blockIdx.x == gridDim.x - 1) {
+        // the extra workgroup: the batch's target count, which needs no
+        // statistics, beside the merge instead of in a launch of its own
+        count_targets<kMergeThreads>(a.target, a.T, a.ignore_index, a.V_total, a.n_valid,
+                                     a.err_count);
+        return;
+    }
     const int64_t r = (int64_t)blockIdx.x * kMergeThreads + threadIdx.x;
     if (r >= a.T) return;
     double M = -__builtin_inf();
@@ -738,9 +755,36 @@ static void stats_dispatch(const StatsArgs &a, bool vec, dim3 grid, hipStream_t 
                            0, stream, a);
 }
 
-hipError_t launch_exp_table(double *tab, hipStream_t stream) {
-    hipLaunchKernelGGL(k_exp_table, dim3((kExpTabN + 255) / 256), dim3(256), 0, stream, tab);
-    return hipGetLastError();
+// The table's device address on the stream's device (each GPU holds its own
+// copy of the code object's array), looked up once per device.
+hipError_t exp_table_address(hipStream_t stream, const double **out) {
+    static std::mutex mu;
+    static const double *addr[kMaxDevices] = {};
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    int dev = cur;
+    if (stream) {
+        hipDevice_t sdev = 0;
+        if ((e = hipStreamGetDevice(stream, &sdev)) != hipSuccess) return e;
+        dev = (int)sdev;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(kExpTable));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        addr[dev] = static_cast<const double *>(p);
+    }
+    *out = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_stats(const StatsArgs &a, int in_dt, bool vec, hipStream_t stream) {
@@ -770,7 +814,7 @@ hipError_t launch_stats(const StatsArgs &a, int in_dt, bool vec, hipStream_t str
 }
 
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream) {
-    const dim3 grid((unsigned)((a.T + kMergeThreads - 1) / kMergeThreads));
+    const dim3 grid((unsigned)((a.T + kMergeThreads - 1) / kMergeThreads + (a.count ? 1 : 0)));
     hipLaunchKernelGGL(k_merge, grid, dim3(kMergeThreads), 0, stream, a);
     return hipGetLastError();
 }

@@ -69,8 +69,8 @@ struct FusedArgs {
     float *loss_rows;
     int reduction;
     float eps;
-    // smoothing, bf16 rows: e^z per bf16 pattern (kExpTabN entries, built by
-    // launch_exp_table), or NULL for fp64 exponentials
+    // smoothing, bf16 rows: e^z per bf16 pattern (kExpTabN entries, the
+    // code object's table, exp_table_address), or NULL for fp64 exponentials
     const double *exp_tab = nullptr;
 };
 
@@ -94,6 +94,7 @@ struct StatsArgs {
 // smoothed statistics of bf16 rows.  Entry 2 off + sign holds the pattern
 // (kExpTabLo + off) | sign << 15, off < kExpTabHalf; the two entries after
 // them (off = kExpTabHalf) are NaN: a read clamped to them marks its sum.
+// gen_exp_table.py writes the values (its LO and HALF are these constants).
 constexpr uint32_t kExpTabLo = 0x3780; // bf16 bits of 2^-16
 constexpr int kExpTabHalf = 3200;      // magnitudes up to 2^9
 constexpr int kExpTabNaN = 2 * kExpTabHalf;
@@ -110,6 +111,11 @@ struct MergeArgs {
     ce_row_stats *stats_out; // merged statistics (or NULL)
     ce_row_final *fin;       // finalize outputs (or NULL)
     float *loss_rows;
+    // count: one more workgroup writes the valid-row count and bad-target
+    // count of the batch (as launch_count does); 0 leaves them alone
+    int count = 0;
+    int32_t *n_valid = nullptr;
+    int32_t *err_count = nullptr;
 };
 
 struct GradArgs {
@@ -251,7 +257,8 @@ hipError_t launch_fused_resident(const FusedArgs &a, int in_dt, int out_dt, int6
 // vec: 16-byte vectors (rows aligned) rather than single elements
 hipError_t launch_stats(const StatsArgs &a, int in_dt, bool vec, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs &a, hipStream_t stream);
-hipError_t launch_exp_table(double *tab, hipStream_t stream);
+// device address of the e^z table (kExpTabN entries) on the stream's device
+hipError_t exp_table_address(hipStream_t stream, const double **out);
 hipError_t launch_grad(const GradArgs &a, int in_dt, int out_dt, bool vec, int64_t T,
                        hipStream_t stream);
 
