@@ -437,14 +437,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
     auto blk_col = [&](int e) { return (e & 1) * 128; };            // first tile column
 
     if constexpr (EPI == GEMM_STATS) {
-        // per row of the tile: max and sum of exp over this tile's columns
-        // with the target left out, the target logit, the sum of all logits
-        char *ex = lbase + 4 * 32 * kPitch * 4;                  // after the slabs
-        int32_t *t_l = reinterpret_cast<int32_t *>(ex);           // [256] target column or -1
-        float *pm = reinterpret_cast<float *>(ex + 1024);         // [2][256] per column half
-        float *ps = reinterpret_cast<float *>(ex + 3072);
-        float *pz = reinterpret_cast<float *>(ex + 5120);
-        float *zt = reinterpret_cast<float *>(ex + 7168);         // [256]
+        // Per row of the tile: max and sum of exp over this tile's columns
+        // with the target left out, the target logit, the sum of all
+        // logits.  Straight from the accumulators: lane l holds, for row
+        // block i and register r, tile row 64 w + 16 i + 4 (l / 16) + r at
+        // the 16 columns 16 j + l % 16, so the 16 lanes of a DPP row hold a
+        // tile row's 256 columns between them: a pass over 16 registers and
+        // a 16-lane reduction, four rows at a time.
+        const int q4 = lane >> 4, cl = lane & 15;
+        int32_t *t_l = reinterpret_cast<int32_t *>(lbase); // [256] target column or -1
         {
             const int64_t r = row0 + tid;
             int32_t tl = -1;
@@ -453,80 +454,93 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
                 if (t >= 0 && t < kTile && col0 + t < g.N) tl = (int32_t)t;
             }
             t_l[tid] = tl;
-            zt[tid] = 0.0f;
-        }
-        // one row-pass step: 8 columns of one row per lane, reduced over the
-        // row's 16 lanes; FULL: every column of the tile is inside N
-        auto row_step = [&](int e, int it, auto FULL) {
-            const int rl = 4 * it + sub;                      // row in the block
-            const int row = blk_row(e) + rl;                  // row in the tile
-            const int cb = blk_col(e) + c8;                   // first column in the tile
-            const float *src = slab + rl * kPitch + c8;
-            const u32x4 p0 = *reinterpret_cast<const u32x4 *>(src);
-            const u32x4 p1 = *reinterpret_cast<const u32x4 *>(src + 4);
-            float z[8];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                z[q] = __uint_as_float(p0[q]);
-                z[4 + q] = __uint_as_float(p1[q]);
-            }
-            const int d = t_l[row] - cb; // the target's place among this lane's columns
-            if (__builtin_expect((unsigned)d < 8u, 0)) {
-                float v = z[0];
-#pragma unroll
-                for (int q = 1; q < 8; ++q) v = (q == d) ? z[q] : v;
-                zt[row] = v;
-            }
-            float mx = ninf(), sz = 0.0f;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const bool in = decltype(FULL)::value || col0 + cb + q < g.N;
-                if (LS && in) sz += z[q];
-                if (!in || q == d) z[q] = ninf();
-                mx = fmaxf(mx, z[q]);
-            }
-            mx = row16_max(mx);
-            float s = 0.0f;
-            if (mx != ninf()) {
-                const float K = mx * kL2E;
-#pragma unroll
-                for (int q = 0; q < 8; ++q) s += fast_exp2(fmaf(z[q], kL2E, -K));
-            }
-            s = row16_sum(s);
-            if (LS) sz = row16_sum(sz);
-            if ((lane & 15) == 0) {
-                pm[(e & 1) * 256 + row] = mx;
-                ps[(e & 1) * 256 + row] = s;
-                pz[(e & 1) * 256 + row] = sz;
-            }
-        };
-        const bool full = col0 + kTile <= g.N;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            __syncthreads();
-            stage(e);
-            __syncthreads();
-            if (full) {
-#pragma unroll 2
-                for (int it = 0; it < 8; ++it) row_step(e, it, std::true_type{});
-            } else {
-                for (int it = 0; it < 8; ++it) row_step(e, it, std::false_type{});
-            }
         }
         __syncthreads();
-        const int64_t r = row0 + tid;
-        if (r < g.M) {
-            const float m0 = pm[tid], m1 = pm[256 + tid];
-            const float M = fmaxf(m0, m1);
-            double s = 0.0;
-            if (m0 != ninf()) s += (double)ps[tid] * exp_nonpos((double)m0 - (double)M);
-            if (m1 != ninf()) s += (double)ps[256 + tid] * exp_nonpos((double)m1 - (double)M);
-            LinTileStats o;
-            o.m = M;
-            o.s = (float)s;
-            o.zt = zt[tid];
-            o.sz = LS ? (float)((double)pz[tid] + (double)pz[256 + tid]) : 0.0f;
-            g.stats[r * g.tiles_n + tn] = o;
+        const bool full = col0 + kTile <= g.N;
+        const int ncol = full ? kTile : (int)(g.N - col0); // columns inside N
+        // pairwise sums and maxima of 16 registers
+        auto tree_sum = [](const float *x) {
+            float a[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) a[k] = x[k] + x[k + 8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) a[k] += a[k + 4];
+            return (a[0] + a[2]) + (a[1] + a[3]);
+        };
+        auto tree_max = [](const float *x) {
+            float a[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) a[k] = fmaxf(x[k], x[k + 8]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) a[k] = fmaxf(a[k], a[k + 4]);
+            return fmaxf(fmaxf(a[0], a[2]), fmaxf(a[1], a[3]));
+        };
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float v[4][16];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) v[r][j] = acc[i][j][r];
+            float m[4], sm[4], sz[4], zt[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (!full) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        if (16 * j + cl >= ncol) v[r][j] = LS ? 0.0f : ninf();
+                }
+                sz[r] = LS ? tree_sum(v[r]) : 0.0f; // every column inside N, the target too
+                if (LS && !full) {
+#pragma unroll
+                    for (int j = 0; j < 16; ++j)
+                        if (16 * j + cl >= ncol) v[r][j] = ninf();
+                }
+                zt[r] = 0.0f;
+                const int tcol = t_l[wave * 64 + 16 * i + 4 * q4 + r];
+                // the target's column is held by the lane with l % 16 = tcol % 16
+                if (__builtin_expect(tcol >= 0 && (tcol & 15) == cl, 0)) {
+                    const int jt = tcol >> 4;
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) {
+                        if (j == jt) {
+                            zt[r] = v[r][j];
+                            v[r][j] = ninf();
+                        }
+                    }
+                }
+                m[r] = tree_max(v[r]);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) m[r] = row16_max(m[r]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float e[16];
+                const float K = m[r] * kL2E;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) e[j] = fast_exp2(fmaf(v[r][j], kL2E, -K));
+                sm[r] = m[r] != ninf() ? tree_sum(e) : 0.0f;
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sm[r] = row16_sum(sm[r]);
+                zt[r] = row16_sum(zt[r]);
+                if (LS) sz[r] = row16_sum(sz[r]);
+            }
+            if (cl == 0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t row = row0 + wave * 64 + 16 * i + 4 * q4 + r;
+                    if (row < g.M) {
+                        LinTileStats o;
+                        o.m = m[r];
+                        o.s = sm[r];
+                        o.zt = zt[r];
+                        o.sz = sz[r];
+                        g.stats[row * g.tiles_n + tn] = o;
+                    }
+                }
+            }
         }
     } else if constexpr (EPI == GEMM_GRAD) {
         // G = k (softmax - q) of the tile, rounded to bf16 (RNE), written in
