@@ -544,16 +544,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
         }
     } else if constexpr (EPI == GEMM_GRAD) {
         // G = k (softmax - q) of the tile, rounded to bf16 (RNE), written in
-        // fragment-major form twice: G (rows = tokens, K = classes) from the
-        // row pass, where a lane holds 8 consecutive classes of one token,
-        // and GT (rows = classes, K = tokens) from a column pass over the
-        // bf16 copy of the block, where a lane gathers 8 consecutive tokens
-        // of one class.
-        constexpr int kBPitch = 136; // bf16 per row of the bf16 slab
-        uint16_t *bslab = reinterpret_cast<uint16_t *>(lbase + 4 * 32 * kPitch * 4) +
-                          wave * 32 * kBPitch;
-        LinRow *rc = reinterpret_cast<LinRow *>(lbase + 4 * 32 * kPitch * 4 +
-                                                4 * 32 * kBPitch * 2);
+        // fragment-major form twice, straight from the accumulators (lane l
+        // holds, for row block i and register r, token 64 w + 16 i + 4 (l/16)
+        // + r of the tile at class 16 j + l % 16):
+        // - GT (rows = classes, K = tokens): a fragment lane needs 8
+        //   consecutive tokens of one class.  Lane groups q hold tokens
+        //   4q .. 4q+3 of row blocks 2b and 2b+1; one v_permlane32_swap and
+        //   one v_permlane16_swap per dword regroup them so that group q'
+        //   holds tokens 8q' .. 8q'+7 of the 32-token block, with no LDS;
+        // - G (rows = tokens, K = classes): neighbouring lanes swap one dword
+        //   (DPP) to form bf16 pairs of adjacent classes of one token, which
+        //   go to the wave's own token-major LDS region and are read back 16
+        //   bytes (8 classes) per lane.
+        constexpr int kGPitch = 528;                  // bytes per token row: 256 classes + 16 (banks)
+        constexpr int kGRegion = 64 * kGPitch;        // one wave's 64 tokens
+        static_assert(4 * kGRegion + kTile * (int)sizeof(LinRow) <= kGemmLdsBytes, "G epilogue LDS");
+        LinRow *rc = reinterpret_cast<LinRow *>(lbase + 4 * kGRegion);
         {
             // rows past M get all-zero constants: valid = 0
             const int64_t r = row0 + tid;
@@ -567,69 +573,113 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &g, int tm, int tn, cha
 #pragma unroll
             for (int q = 0; q < 3; ++q) dst[q] = v[q];
         }
+        __syncthreads();
         char *GT = reinterpret_cast<char *>(g.GT);
         char *G = reinterpret_cast<char *>(g.G);
+        char *greg = lbase + wave * kGRegion;
+        const int q4 = lane >> 4, cl = lane & 15;
+        const bool odd = (cl & 1) != 0;
+        const bool full = col0 + kTile <= g.N;
+        const int ncol = full ? kTile : (int)(g.N - col0); // classes inside N
         // gradient filtering: whether this lane saw an entry of a valid row
         // with k != 0 and |G| >= filter_eps |k| (|p - q| >= filter_eps
         // unscaled); a row with k = 0 has an all-zero gradient and keeps
         // nothing
         bool kept = false;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            __syncthreads();
-            stage(e);
-            __syncthreads();
-#pragma unroll 2
-            for (int it = 0; it < 8; ++it) {
-                const int rl = 4 * it + sub;
-                const int64_t n = row0 + blk_row(e) + rl;
-                const int64_t v0 = col0 + blk_col(e) + c8;
-                const float *src = slab + rl * kPitch + c8;
-                const u32x4 p0 = *reinterpret_cast<const u32x4 *>(src);
-                const u32x4 p1 = *reinterpret_cast<const u32x4 *>(src + 4);
-                const LinRow R = rc[blk_row(e) + rl];
-                const int64_t tcl = (int64_t)R.t - g.col_base;
-                float gv[8];
+        for (int tb = 0; tb < 2; ++tb) {
+            // D[ii][j]: tokens (4q, 4q+1) and (4q+2, 4q+3) of row block
+            // 2 tb + ii at class 16 j + l % 16, as bf16 pairs
+            uint32_t D[2][16][2];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float z = __uint_as_float(e < 4 ? p0[e] : p1[e - 4]);
-                    const int64_t v = v0 + e;
-                    float x = 0.0f;
-                    if (R.valid && v < g.N)
-                        x = (v == tcl) ? R.c.gk : grad_elem<CE_BF16, LS>(z, R.c);
-                    gv[e] = x;
+            for (int ii = 0; ii < 2; ++ii) {
+                const int i = 2 * tb + ii;
+                float gv[4][16];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const LinRow R = rc[wave * 64 + 16 * i + 4 * q4 + r];
+#pragma unroll
+                    for (int j = 0; j < 16; ++j) gv[r][j] = grad_elem<CE_BF16, LS>(acc[i][j][r], R.c);
+                    if (!full) {
+#pragma unroll
+                        for (int j = 0; j < 16; ++j)
+                            if (16 * j + cl >= ncol) gv[r][j] = 0.0f;
+                    }
+                    // the target's class is held by the lane with l % 16 = t % 16
+                    const int64_t tcl = (int64_t)R.t - g.col_base - col0;
+                    if (__builtin_expect(tcl >= 0 && tcl < ncol && (int)(tcl & 15) == cl, 0)) {
+                        const int jt = (int)(tcl >> 4);
+#pragma unroll
+                        for (int j = 0; j < 16; ++j)
+                            if (j == jt) gv[r][j] = R.c.gk;
+                    }
+                    if (!R.valid) {
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) gv[r][j] = 0.0f;
+                    }
+                    if constexpr (FILT) {
+                        const float thr = g.filter_eps * fabsf(R.c.k);
+                        float mx = 0.0f;
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(gv[r][j]));
+                        kept = kept || (R.valid && R.c.k != 0.0f && mx >= thr);
+                    }
                 }
-                if constexpr (FILT) {
-                    const float thr = g.filter_eps * fabsf(R.c.k);
-                    float mx = 0.0f;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(gv[e]));
-                    kept = kept || (R.valid && R.c.k != 0.0f && mx >= thr);
+                for (int j = 0; j < 16; ++j) {
+                    D[ii][j][0] = pack_bf16x2(gv[0][j], gv[1][j]);
+                    D[ii][j][1] = pack_bf16x2(gv[2][j], gv[3][j]);
                 }
-                u32x4 w;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(gv[2 * e], gv[2 * e + 1]);
-                *reinterpret_cast<u32x4 *>(bslab + rl * kBPitch + c8) = w;
-                const int64_t off = frag_off(n >> 4, v0 >> 5, g.ldg) +
-                                    (int64_t)((n & 15) + 16 * ((v0 & 31) >> 3)) * 16;
-                *reinterpret_cast<u32x4 *>(G + off) = w;
             }
-            __syncthreads();
-            // column pass: fragment f*64 + lane = (class c, tokens 8 tau .. +7)
-#pragma unroll 2
-            for (int f = 0; f < 8; ++f) {
-                const int phi = f * 64 + lane;
-                const int c = phi & 127, tau = phi >> 7;
-                u32x4 w;
+            // GT fragments of the 32-token block tb: class block j, lane l
+            // at byte 16 l of the fragment (class l % 16, tokens 8 (l/16) ..)
+            const int64_t n0 = row0 + wave * 64 + 32 * tb;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[e] = (uint32_t)bslab[(8 * tau + 2 * e) * kBPitch + c] |
-                           ((uint32_t)bslab[(8 * tau + 2 * e + 1) * kBPitch + c] << 16);
-                const int64_t v = col0 + blk_col(e) + c;
-                const int64_t n0 = row0 + blk_row(e) + 8 * tau;
-                const int64_t off = frag_off(v >> 4, n0 >> 5, g.ldgt) +
-                                    (int64_t)((v & 15) + 16 * ((n0 & 31) >> 3)) * 16;
-                *reinterpret_cast<u32x4 *>(GT + off) = w;
+            for (int j = 0; j < 16; ++j) {
+                const auto s0 = __builtin_amdgcn_permlane32_swap(D[0][j][0], D[1][j][0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(D[0][j][1], D[1][j][1], false, false);
+                const auto x0 = __builtin_amdgcn_permlane16_swap(s0[0], s0[1], false, false);
+                const auto x1 = __builtin_amdgcn_permlane16_swap(s1[0], s1[1], false, false);
+                const u32x4 w = {(uint32_t)x0[0], (uint32_t)x1[0], (uint32_t)x0[1], (uint32_t)x1[1]};
+                const int64_t c = col0 + 16 * j;
+                *reinterpret_cast<u32x4 *>(GT + frag_off(c >> 4, n0 >> 5, g.ldgt) + lane * 16) = w;
+            }
+            // G: pairs of adjacent classes of one token into the LDS region;
+            // an even lane writes tokens 4q, 4q+1 at classes (c, c+1), an
+            // odd lane tokens 4q+2, 4q+3 at classes (c-1, c)
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+                const int tok = 16 * (2 * tb + ii) + 4 * q4 + (odd ? 2 : 0);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const uint32_t p0 = D[ii][j][0], p1 = D[ii][j][1];
+                    const uint32_t give = odd ? p0 : p1, own = odd ? p1 : p0;
+                    const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, 0xB1, 0xf, 0xf, false);
+                    const uint32_t lo = odd ? got : own, hi = odd ? own : got; // lower class first
+                    const uint32_t w0 = (lo & 0xffffu) | (hi << 16);
+                    const uint32_t w1 = (lo >> 16) | (hi & 0xffff0000u);
+                    char *d = greg + tok * kGPitch + (16 * j + (cl & ~1)) * 2;
+                    *reinterpret_cast<uint32_t *>(d) = w0;
+                    *reinterpret_cast<uint32_t *>(d + kGPitch) = w1;
+                }
+            }
+        }
+        // the region is this wave's alone: its LDS writes and reads stay in
+        // order, and the compiler may not move the reads above the writes
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // G fragments: token block tk (16 tokens), class block s (32
+        // classes), lane l at byte 16 l (token l % 16, classes 8 (l/16) ..)
+#pragma unroll
+        for (int tk = 0; tk < 4; ++tk) {
+            const int64_t n = row0 + wave * 64 + 16 * tk;
+#pragma unroll
+            for (int sb = 0; sb < 8; ++sb) {
+                const u32x4 w = *reinterpret_cast<const u32x4 *>(
+                    greg + (16 * tk + cl) * kGPitch + (32 * sb + 8 * q4) * 2);
+                const int64_t v0 = col0 + 32 * sb;
+                *reinterpret_cast<u32x4 *>(G + frag_off(n >> 4, v0 >> 5, g.ldg) + lane * 16) = w;
             }
         }
         if constexpr (FILT) {
