@@ -377,10 +377,12 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
     // One vector of 8 logits, branch-free, so that a group's vectors keep all
     // their table reads in flight together.  Two logits are handled at a
     // time in the 16-bit lanes of a word:
-    // - table byte offset: off = |pattern| - kExpTabLo (wrapping below),
-    //   clamped to kExpTabHalf (the NaN entries), times 16, plus 8 for a
-    //   negative logit; a pattern outside the table thus makes the vector's
-    //   sum NaN, which the caller tests once per vector;
+    // - table byte offset: the pattern rotated left by one bit is
+    //   2 |pattern| + sign (one packed multiply-add of the pattern by 2 and
+    //   its sign bit); minus 2 kExpTabLo (wrapping below) that is the entry
+    //   index 2 off + sign, clamped to 2 kExpTabHalf (a NaN entry), times 8;
+    //   a pattern outside the table thus makes the vector's sum NaN, which
+    //   the caller tests once per vector;
     // - max: a running max of the patterns read as fp16 numbers.  Like
     //   bf16, fp16 orders sign-magnitude patterns as their values, so the
     //   largest fp16 reading is the largest logit, for every pattern in the
@@ -397,11 +399,15 @@ __device__ __forceinline__ void stats_tab_unit(const StatsArgs &a, int64_t unit,
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const uint32_t w = v.v[q];
-            const u16x2 off = __builtin_bit_cast(u16x2, w & 0x7fff7fffu) - (u16x2)(uint16_t)kExpTabLo;
-            const u16x2 c = __builtin_elementwise_min(off, (u16x2)(uint16_t)kExpTabHalf);
-            uint32_t a2 = __builtin_bit_cast(uint32_t, c << (uint16_t)4) | ((w >> 12) & 0x00080008u);
-            // one and-or per word: without this fence the compiler forms the
-            // low offset in a separate operation
+            // the compiler builds x * 2 + (x >> 15) from a shift, a shift
+            // and an or; v_pk_mad_u16 does it in one operation
+            const uint32_t sg = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, w) >> (uint16_t)15);
+            uint32_t rot;
+            asm("v_pk_mad_u16 %0, %1, %2, %3" : "=v"(rot) : "v"(w), "v"(0x00020002u), "v"(sg));
+            const u16x2 ix = __builtin_bit_cast(u16x2, rot) - (u16x2)(uint16_t)(2 * kExpTabLo);
+            const u16x2 c = __builtin_elementwise_min(ix, (u16x2)(uint16_t)(2 * kExpTabHalf));
+            uint32_t a2 = __builtin_bit_cast(uint32_t, c << (uint16_t)3);
+            // keeps the two offsets to one and and one shift
             asm("" : "+v"(a2));
             t[2 * q] = *reinterpret_cast<const double *>(tabc + (a2 & 0xffffu));
             t[2 * q + 1] = *reinterpret_cast<const double *>(tabc + (a2 >> 16));
