@@ -483,18 +483,24 @@ int fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtype,
         return CE_ERR_ALIAS;
 
     int32_t *nv = n_valid ? n_valid : at<int32_t>(ws, l.n_valid);
-    VCE_TRY(launch_count(target, p.T, p.ignore_index, p.V_total, nv, err_count, s));
     float *lr = loss_rows ? loss_rows : at<float>(ws, l.loss_rows);
+    const bool vec = p.T > 0 && vec_ok(logits, p.ld, logits_dtype, grad, ldg, grad_dtype);
+    const bool svec = p.T > 0 && stream_vec_ok(logits, p.ld, logits_dtype, grad, ldg, grad_dtype);
+    const bool split = p.T < kResidentMinRows && p.V_local >= kResidentSplitCols;
+    const bool smoothed_long = p.label_smoothing > 0.0f && logits_dtype == CE_BF16 &&
+                               p.V_local > kSmoothedResidentMaxCols;
+    const bool resident = p.T > 0 && svec && !split && !smoothed_long &&
+                          fused_fits(logits_dtype, p.V_local, vec, p.label_smoothing > 0.0f);
+    // The count of valid targets comes first, from its own launch, except
+    // where a later kernel of this call takes it over: a small batch's
+    // register-resident kernel, or the merge of the streaming form.
+    const bool count_inline = resident && p.T <= kInlineCountMaxRows;
+    if (p.T == 0 || (resident && !count_inline))
+        VCE_TRY(launch_count(target, p.T, p.ignore_index, p.V_total, nv, err_count, s));
 
     if (p.T > 0 && ev_start) VCE_TRY(hipEventRecord(ev_start, s));
     if (p.T > 0) {
-        const bool vec = vec_ok(logits, p.ld, logits_dtype, grad, ldg, grad_dtype);
-        const bool svec = stream_vec_ok(logits, p.ld, logits_dtype, grad, ldg, grad_dtype);
-        const bool split = p.T < kResidentMinRows && p.V_local >= kResidentSplitCols;
-        const bool smoothed_long = p.label_smoothing > 0.0f && logits_dtype == CE_BF16 &&
-                                   p.V_local > kSmoothedResidentMaxCols;
-        if (svec && !split && !smoothed_long &&
-            fused_fits(logits_dtype, p.V_local, vec, p.label_smoothing > 0.0f)) {
+        if (resident) {
             FusedArgs fa;
             fa.logits = logits;
             fa.ld = p.ld;
@@ -509,6 +515,10 @@ int fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtype,
             fa.reduction = p.reduction;
             fa.eps = p.label_smoothing;
             fa.exp_tab = nullptr;
+            fa.count_inline = count_inline ? 1 : 0;
+            fa.T = p.T;
+            fa.count_out = nv;
+            fa.err_out = err_count;
             if (p.label_smoothing > 0.0f && fused_table(logits_dtype, p.V_local)) {
                 // the smoothed sums read e^z from the code object's table
                 VCE_TRY(exp_table_address(s, &fa.exp_tab));
@@ -547,6 +557,10 @@ int fused_fwd_bwd(const ce_problem *prob, const void *logits, int logits_dtype,
             ma.stats_out = nullptr;
             ma.fin = fin;
             ma.loss_rows = lr;
+            // the target count runs as one more workgroup of the merge
+            ma.count = 1;
+            ma.n_valid = nv;
+            ma.err_count = err_count;
             VCE_TRY(launch_merge(ma, s));
 
             GradArgs ga;

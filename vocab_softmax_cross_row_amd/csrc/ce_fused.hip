@@ -85,6 +85,53 @@ __device__ __forceinline__ double tab_exp8_slow(const u32x4 &w, const double *ta
 // fp64 finalize.  TAB (bf16 with smoothing): the fp64 sum of exponentials
 // reads e^z from the LDS table `tab` instead of an fp64 exponential per
 // logit.
+// The batch's count of valid and of bad targets, by one workgroup (every
+// thread gets both): small batches count in the fused kernel itself.
+template <int THREADS>
+__device__ __forceinline__ void inline_count(const FusedArgs &a, int &n_valid, int &n_bad) {
+    int nv = 0, nb = 0;
+    for (int64_t r = threadIdx.x; r < a.T; r += THREADS) {
+        const int64_t t = a.target[r];
+        if (t == a.ignore_index) continue;
+        if (t >= 0 && t < a.V)
+            ++nv;
+        else
+            ++nb;
+    }
+    nv = wave_sum(nv);
+    nb = wave_sum(nb);
+    __shared__ int part[2][THREADS / kWave];
+    const int wv = threadIdx.x / kWave;
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        part[0][wv] = nv;
+        part[1][wv] = nb;
+    }
+    __syncthreads();
+    n_valid = n_bad = 0;
+#pragma unroll
+    for (int i = 0; i < THREADS / kWave; ++i) {
+        n_valid += part[0][i];
+        n_bad += part[1][i];
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *a.count_out = n_valid;
+        if (a.err_out) *a.err_out = n_bad;
+    }
+}
+
+// Scale k_r of a row's gradient from a count already at hand.
+__device__ __forceinline__ double row_scale_n(int reduction, const float *grad_output, int n_valid,
+                                              int64_t row) {
+    double g = 1.0;
+    if (reduction == CE_RED_NONE) {
+        if (grad_output) g = (double)grad_output[row];
+        return g;
+    }
+    if (grad_output) g = (double)grad_output[0];
+    if (reduction == CE_RED_MEAN) g /= (double)n_valid;
+    return g;
+}
+
 template <int IN, int OUT, int THREADS, int NV, bool LS, bool TAB>
 __device__ __forceinline__ void fused_row(const FusedArgs &a, int64_t row,
                                           BlockRed<THREADS> &red, GradConst &gc_sh,
@@ -116,7 +163,12 @@ __device__ __forceinline__ void fused_row(const FusedArgs &a, int64_t row,
 
     const int64_t t64 = a.target[row];
     if (t64 == a.ignore_index || t64 < 0 || t64 >= V) {
-        // ignored row or bad target: zero gradient, no reads of the row
+        // ignored row or bad target: zero gradient, no reads of the row;
+        // workgroup 0 still writes the batch's count
+        if (a.count_inline && blockIdx.x == 0) {
+            int nv, nb;
+            inline_count<THREADS>(a, nv, nb);
+        }
         float zero[EPV];
 #pragma unroll
         for (int e = 0; e < EPV; ++e) zero[e] = 0.0f;
@@ -158,6 +210,11 @@ __device__ __forceinline__ void fused_row(const FusedArgs &a, int64_t row,
                     rt, (__attribute__((address_space(3))) void *)(tv + q * THREADS + wave_base), 16,
                     (q * THREADS + tid) * 16, 0, 0, 0);
     }
+
+    // the batch's count, counted here while the row's loads are in flight
+    int n_valid = 0, n_bad = 0;
+    if (a.count_inline && (blockIdx.x == 0 || a.reduction == CE_RED_MEAN))
+        inline_count<THREADS>(a, n_valid, n_bad);
 
     // where the target sits: vector tv = slot t_slot of thread t_thread
     // (wave t_wave), element te; or the scalar tail.  t is the same for the
@@ -293,7 +350,8 @@ __device__ __forceinline__ void fused_row(const FusedArgs &a, int64_t row,
     // ---- finalize (one thread) -----------------------------------------------
     if (tid == 0) {
         const float zt = In::load1(zrow + (int64_t)t * In::kSize);
-        const double k = row_scale(a.reduction, a.grad_output, a.n_valid, row);
+        const double k = a.count_inline ? row_scale_n(a.reduction, a.grad_output, n_valid, row)
+                                        : row_scale(a.reduction, a.grad_output, a.n_valid, row);
         if constexpr (FAST) {
             const FastFinal f = finalize_fast(mx, s, zt, k);
             a.loss_rows[row] = f.loss;
@@ -730,11 +788,19 @@ hipError_t launch_fused_resident(const FusedArgs &a, int in_dt, int out_dt, int6
     // the register-resident kernel, which peels their heads
     const int lds = (ls || !aligned) ? 0 : lds_split_bytes(in_dt, a.V);
     if (lds > 0) {
+        // this kernel reads the count from n_valid
+        FusedArgs b = a;
+        if (b.count_inline) {
+            const hipError_t e = launch_count(a.target, a.T, a.ignore_index, a.V, a.count_out,
+                                              a.err_out, stream);
+            if (e != hipSuccess) return e;
+            b.count_inline = 0;
+        }
         if (in_dt == CE_BF16)
-            return out_dt == CE_BF16 ? launch_lds<CE_BF16, CE_BF16>(a, T, lds, stream)
-                                     : launch_lds<CE_BF16, CE_F32>(a, T, lds, stream);
-        return out_dt == CE_BF16 ? launch_lds<CE_F32, CE_BF16>(a, T, lds, stream)
-                                 : launch_lds<CE_F32, CE_F32>(a, T, lds, stream);
+            return out_dt == CE_BF16 ? launch_lds<CE_BF16, CE_BF16>(b, T, lds, stream)
+                                     : launch_lds<CE_BF16, CE_F32>(b, T, lds, stream);
+        return out_dt == CE_BF16 ? launch_lds<CE_F32, CE_BF16>(b, T, lds, stream)
+                                 : launch_lds<CE_F32, CE_F32>(b, T, lds, stream);
     }
     if (in_dt == CE_BF16) {
         if (out_dt == CE_BF16)

@@ -72,7 +72,20 @@ struct FusedArgs {
     // smoothing, bf16 rows: e^z per bf16 pattern (kExpTabN entries, the
     // code object's table, exp_table_address), or NULL for fp64 exponentials
     const double *exp_tab = nullptr;
+    // count_inline (batches of at most kInlineCountMaxRows rows): each
+    // workgroup counts the batch's T targets itself instead of reading
+    // n_valid, and workgroup 0 writes the count to count_out and the bad
+    // targets to err_out (if not NULL), so no count launch precedes the
+    // kernel.  The register-resident kernels only: launch_fused_resident
+    // launches the count itself before the LDS-split kernel.
+    int count_inline = 0;
+    int64_t T = 0;
+    int32_t *count_out = nullptr;
+    int32_t *err_out = nullptr;
 };
+// Up to this many rows a workgroup reads every target of the batch (8 KB)
+// rather than wait for a count launch.
+constexpr int64_t kInlineCountMaxRows = 1024;
 
 struct StatsArgs {
     const void *logits;
