@@ -660,12 +660,15 @@ namespace vce {
 // row left half of its threads idle (65536 x 1000 bf16: 157 us at 256 x 1,
 // 85 us at 64 x 2).  With smoothing the fp64 work per logit makes 64-thread
 // workgroups pay up to 4096 columns (65536 x 4096: 381 -> 333 us); without
-// it 256 x 2 stays best there (204 against 215 us).
+// it 256 x 2 stays best there (204 against 215 us).  Rows of 8K to 32K
+// columns without smoothing take 512 threads (65536 x 12000 bf16: 567 ->
+// 546 us at 512 x 4; 65536 x 32000: 1453 -> 1432 us at 512 x 8); 512 x 2
+// was slower at 6000 columns, and with smoothing 512 x 4 was slower.
 struct ResidentShape {
     int threads, nv;
 };
 constexpr ResidentShape kResident[] = {{64, 1},   {64, 2},   {128, 2},   {256, 2}, {256, 4},
-                                       {256, 8},  {256, 16}, {512, 16},  {1024, 16}};
+                                       {512, 4},  {512, 8},  {512, 16},  {1024, 16}};
 constexpr ResidentShape kResidentLS[] = {{64, 1},  {64, 2},   {64, 4},    {64, 8},  {256, 4},
                                          {256, 8}, {256, 16}, {512, 16},  {1024, 16}};
 constexpr int kNumResident = sizeof(kResident) / sizeof(kResident[0]);
@@ -715,8 +718,8 @@ static hipError_t fused_dispatch(const FusedArgs &a, int64_t T, hipStream_t stre
         case 2: VCE_RES(128, 2)
         case 3: VCE_RES(256, 2)
         case 4: VCE_RES(256, 4)
-        case 5: VCE_RES(256, 8)
-        case 6: VCE_RES(256, 16)
+        case 5: VCE_RES(512, 4)
+        case 6: VCE_RES(512, 8)
         case 7: VCE_RES(512, 16)
         case 8: VCE_RES(1024, 16)
         default: return hipErrorInvalidValue;
