@@ -397,6 +397,20 @@ def test_bad_targets_counted():
     assert math.isnan(out["loss"].item())
 
 
+@pytest.mark.parametrize("T", [5, 1024, 1025])
+def test_batch_count_in_kernel_and_by_launch(T):
+    """Batches of up to 1024 rows on the register-resident kernel count their
+    targets inside it (workgroup 0, which takes row 0, writes the count);
+    longer ones in a launch of their own.  Row 0 holds a bad target, so the
+    workgroup writing the count takes the zero-gradient exit; the mean
+    reduction makes every gradient row depend on the count."""
+    c, logits, target = _case(S.MID, T, 3000, 11)
+    target[0] = 3000
+    target[1::7] = c.ignore_index
+    c = dataclasses.replace(c, reduction="mean")
+    _fused_check(c, logits, target, what=f"count T={T}")
+
+
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
 def test_minus_inf_logits(dt):
     """Rows with -inf fallback logits (torchtitan PR Test Plan)."""
