@@ -330,8 +330,10 @@ int ce_version(void);
 
 /* ce_fused_fwd_bwd, plus two HIP events (hipEvent_t handles created and
  * owned by the caller, passed as void *) recorded on `stream`: ev_start just
- * before the call's main kernels (after the count of valid targets) and
- * ev_stop just after them (before the loss reduction), so that a benchmark
+ * before the call's main kernels (after the count of valid targets when
+ * that is a launch of its own; batches of at most 1024 rows on the
+ * register-resident kernels count inside them) and ev_stop just after them
+ * (before the loss reduction), so that a benchmark
  * can time the fused kernel alone with hipEventElapsedTime.  Both NULL: the
  * same as ce_fused_fwd_bwd.  CE_ERR_ARG if exactly one is NULL.  Results
  * are bit-identical to ce_fused_fwd_bwd; the library keeps no state. */
